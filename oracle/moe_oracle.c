@@ -1,0 +1,402 @@
+/*
+ * moe_oracle.c -- plain fp64 CPU oracle of one MoE layer's routed-expert forward
+ * pass.  TEST INFRASTRUCTURE ONLY (tests, smoke check, bench CPU baseline).
+ *
+ * Pages: "Meet FreeToken: An Edge-Native MoE Serving Engine that Runs 753B GLM-5.2
+ * on a Single Workstation GPU" (MarkTechPost).  The pages state the system's
+ * policies (route without modifying the router, a shared LRU expert cache spanning
+ * all MoE layers, a cold start, bit-exact expert output) but print no layer
+ * equation; every formula here is the textbook definition of the step, and each
+ * reading the pages leave open is named where it is taken.
+ *
+ * Everything is written for obviousness, not speed: straight loops, fp64, no
+ * blocking or reordering.
+ */
+#include "moe_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ===========================================================================
+ * Stored formats
+ * ======================================================================== */
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+double ora_bf16_value(uint16_t bits) {
+  uint32_t u = ((uint32_t)bits) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* E2M1 element of OCP Microscaling Formats (MX) v1.0 (the pages name the MXFP4
+ * build in the section "Results").  Bit 3 is the sign; codes 0..7 carry the
+ * magnitudes of the spec's E2M1 table. */
+double ora_e2m1_value(uint8_t code) {
+  static const double magnitude[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  double v = magnitude[code & 7u];
+  return (code & 8u) ? -v : v;
+}
+
+/* E8M0 block scale of OCP MX v1.0: 2^(code - 127); code 0xFF encodes NaN. */
+double ora_e8m0_value(uint8_t code) {
+  if (code == 0xFFu) return NAN;
+  return ldexp(1.0, (int)code - 127);
+}
+
+size_t ora_expert_bytes(int dtype, int H, int I) {
+  size_t n = (size_t)3 * (size_t)H * (size_t)I;
+  switch (dtype) {
+    case ORA_F32: return 4 * n;
+    case ORA_BF16: return 2 * n;
+    case ORA_MXFP4: return n / 2 + n / 32;
+    default: return 0;
+  }
+}
+
+/* Element (r, c) of a rows x K matrix stored at `p` in `dtype`.
+ * MXFP4 (a reading: the pages only say "MXFP4"): blocks of 32 along K, element
+ * 2i in the low nibble of byte i of the row, scales row-major [rows][K/32] in a
+ * separate array `s`. */
+static double element(int dtype, const uint8_t* p, const uint8_t* s, int K, int r, int c) {
+  size_t idx = (size_t)r * (size_t)K + (size_t)c;
+  if (dtype == ORA_F32) {
+    float f;
+    memcpy(&f, p + 4 * idx, sizeof f);
+    return (double)f;
+  }
+  if (dtype == ORA_BF16) {
+    uint16_t b;
+    memcpy(&b, p + 2 * idx, sizeof b);
+    return ora_bf16_value(b);
+  }
+  {
+    uint8_t byte = p[(size_t)r * (size_t)(K / 2) + (size_t)(c / 2)];
+    uint8_t code = (c % 2 == 0) ? (uint8_t)(byte & 0x0Fu) : (uint8_t)(byte >> 4);
+    uint8_t scale = s[(size_t)r * (size_t)(K / 32) + (size_t)(c / 32)];
+    return ora_e2m1_value(code) * ora_e8m0_value(scale);
+  }
+}
+
+/* Slot layout ("final host layout", one contiguous run per expert):
+ *   f32/bf16: W13 [2I][H] then W2 [H][I]
+ *   mxfp4:    W13 codes [2I][H/2], W2 codes [H][I/2], W13 scales [2I][H/32], W2 scales [H][I/32]
+ * Rows 0..I-1 of W13 are the gate projection, rows I..2I-1 the up projection. */
+int ora_decode_expert(int dtype, const uint8_t* slot, int H, int I, double* wg, double* wu, double* wd) {
+  const uint8_t *w13, *w2, *s13 = NULL, *s2 = NULL;
+  if (H <= 0 || I <= 0) return -1;
+  if (dtype == ORA_F32 || dtype == ORA_BF16) {
+    size_t esz = dtype == ORA_F32 ? 4 : 2;
+    w13 = slot;
+    w2 = slot + esz * 2 * (size_t)I * (size_t)H;
+  } else if (dtype == ORA_MXFP4) {
+    if (H % 32 || I % 32) return -1;
+    w13 = slot;
+    w2 = w13 + (size_t)I * (size_t)H;         /* 2I rows x H/2 bytes */
+    s13 = w2 + (size_t)H * (size_t)I / 2;      /* H rows x I/2 bytes */
+    s2 = s13 + (size_t)2 * I * (size_t)(H / 32);
+  } else {
+    return -1;
+  }
+  for (int j = 0; j < I; ++j)
+    for (int h = 0; h < H; ++h) {
+      wg[(size_t)j * H + h] = element(dtype, w13, s13, H, j, h);
+      wu[(size_t)j * H + h] = element(dtype, w13, s13, H, I + j, h);
+    }
+  for (int h = 0; h < H; ++h)
+    for (int j = 0; j < I; ++j) wd[(size_t)h * I + j] = element(dtype, w2, s2, I, h, j);
+  return 0;
+}
+
+int ora_decode_x(int dtype, const void* x, int T, int H, double* out) {
+  size_t n = (size_t)T * (size_t)H;
+  if (dtype == ORA_F32) {
+    const float* f = (const float*)x;
+    for (size_t i = 0; i < n; ++i) out[i] = (double)f[i];
+  } else if (dtype == ORA_BF16 || dtype == ORA_MXFP4) {
+    const uint16_t* b = (const uint16_t*)x;
+    for (size_t i = 0; i < n; ++i) out[i] = ora_bf16_value(b[i]);
+  } else {
+    return -1;
+  }
+  return 0;
+}
+
+/* ===========================================================================
+ * Routing
+ * ======================================================================== */
+
+/* Does (va, a) rank before (vb, b)?  Larger logit first; equal logits (IEEE
+ * equality, so -0.0 == +0.0) go to the lower expert index.  The pages require
+ * routing to be left unmodified ("Three mechanisms", bandwidth-adaptive
+ * execution; "Key Takeaways"); the tie-break is the lowest-index reading. */
+static int ranks_before(float va, int a, float vb, int b) {
+  if (va > vb) return 1;
+  if (va < vb) return 0;
+  return a < b;
+}
+
+/* Gate weights are the softmax over the k selected logits, which in exact
+ * arithmetic equals a softmax over all E followed by renormalising the k
+ * selected probabilities. */
+int ora_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w32, double* w64) {
+  if (T < 0 || E <= 0 || k <= 0 || k > E) return -1;
+  char* taken = (char*)malloc((size_t)E);
+  double* z = (double*)malloc(sizeof(double) * (size_t)k);
+  if (!taken || !z) { free(taken); free(z); return -3; }
+  for (int t = 0; t < T; ++t) {
+    const float* row = logits + (size_t)t * E;
+    for (int e = 0; e < E; ++e)
+      if (!isfinite(row[e])) { free(taken); free(z); return -2; }
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || ranks_before(row[e], e, row[best], best)) best = e;
+      }
+      taken[best] = 1;
+      ids[(size_t)t * k + j] = best;
+      z[j] = (double)row[best];
+    }
+    double zmax = z[0];
+    double denom = 0.0;
+    for (int j = 0; j < k; ++j) denom += exp(z[j] - zmax);
+    for (int j = 0; j < k; ++j) {
+      double wj = exp(z[j] - zmax) / denom;
+      if (w64) w64[(size_t)t * k + j] = wj;
+      if (w32) w32[(size_t)t * k + j] = (float)wj;
+    }
+  }
+  free(taken);
+  free(z);
+  return 0;
+}
+
+/* counts[e] = #{r : ids[r] == e}; offsets = exclusive prefix sum (E+1 entries);
+ * sorted_rows lists r grouped by expert, ascending r within an expert;
+ * inv_rows[r] is the position of r in sorted_rows. */
+int ora_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                int32_t* sorted_rows, int32_t* inv_rows) {
+  int n = T * k;
+  if (T < 0 || k <= 0 || E <= 0) return -1;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int r = 0; r < n; ++r) {
+    if (ids[r] < 0 || ids[r] >= E) return -1;
+    counts[ids[r]]++;
+  }
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+  if (!next) return -3;
+  for (int e = 0; e < E; ++e) next[e] = offsets[e];
+  for (int r = 0; r < n; ++r) {
+    int p = next[ids[r]]++;
+    sorted_rows[p] = r;
+    inv_rows[r] = p;
+  }
+  free(next);
+  return 0;
+}
+
+/* ===========================================================================
+ * Expert FFN (SwiGLU) and combine
+ * ======================================================================== */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+void ora_expert_ffn(const double* wg, const double* wu, const double* wd, int H, int I,
+                    const double* x, double* o) {
+  double* h = (double*)malloc(sizeof(double) * (size_t)I);
+  for (int j = 0; j < I; ++j) {
+    double a = 0.0, b = 0.0;
+    for (int c = 0; c < H; ++c) {
+      a += wg[(size_t)j * H + c] * x[c];
+      b += wu[(size_t)j * H + c] * x[c];
+    }
+    h[j] = silu(a) * b;
+  }
+  for (int r = 0; r < H; ++r) {
+    double acc = 0.0;
+    for (int j = 0; j < I; ++j) acc += wd[(size_t)r * I + j] * h[j];
+    o[r] = acc;
+  }
+  free(h);
+}
+
+/* The pages say the partial sums of the routed experts merge exactly ("Three
+ * mechanisms"); the merge is the gate-weighted sum, plus the shared expert with
+ * weight 1 when the layer has one. */
+void ora_combine(const double* rows, const double* w, const double* shared, int T, int k, int H, double* y) {
+  for (int t = 0; t < T; ++t)
+    for (int c = 0; c < H; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) acc += w[(size_t)t * k + j] * rows[((size_t)t * k + j) * H + c];
+      if (shared) acc += shared[(size_t)t * H + c];
+      y[(size_t)t * H + c] = acc;
+    }
+}
+
+int ora_expert_rows(int dtype, const uint8_t* slot, int H, int I, const void* x, int T,
+                    const int32_t* tokens, int n, double* o) {
+  double* wg = (double*)malloc(sizeof(double) * (size_t)I * H);
+  double* wu = (double*)malloc(sizeof(double) * (size_t)I * H);
+  double* wd = (double*)malloc(sizeof(double) * (size_t)H * I);
+  double* xt = (double*)malloc(sizeof(double) * (size_t)H);
+  int rc = 0;
+  if (!wg || !wu || !wd || !xt) { rc = -3; goto done; }
+  rc = ora_decode_expert(dtype, slot, H, I, wg, wu, wd);
+  if (rc) goto done;
+  for (int i = 0; i < n; ++i) {
+    int t = tokens[i];
+    if (t < 0 || t >= T) { rc = -1; goto done; }
+    if (dtype == ORA_F32)
+      ora_decode_x(dtype, (const float*)x + (size_t)t * H, 1, H, xt);
+    else
+      ora_decode_x(dtype, (const uint16_t*)x + (size_t)t * H, 1, H, xt);
+    ora_expert_ffn(wg, wu, wd, H, I, xt, o + (size_t)i * H);
+  }
+done:
+  free(wg); free(wu); free(wd); free(xt);
+  return rc;
+}
+
+int ora_layer(int dtype, const uint8_t* const* expert_ptr, const uint8_t* shared, int I_shared,
+              const void* x, const float* logits, int T, int H, int I, int E, int k,
+              double* y, int32_t* ids, double* w, double* rows, double* shared_out) {
+  int rc = ora_route_topk(logits, T, E, k, ids, NULL, w);
+  if (rc) return rc;
+  double* own_rows = rows ? rows : (double*)malloc(sizeof(double) * (size_t)T * k * H);
+  double* sh = NULL;
+  if (!own_rows) return -3;
+  /* Each routed expert that any token selected, in expert order. */
+  for (int e = 0; e < E && rc == 0; ++e) {
+    int n = 0;
+    for (int r = 0; r < T * k; ++r) n += ids[r] == e;
+    if (!n) continue;
+    int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    int32_t* pair = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    double* o = (double*)malloc(sizeof(double) * (size_t)n * H);
+    int m = 0;
+    for (int r = 0; r < T * k; ++r)
+      if (ids[r] == e) { tok[m] = r / k; pair[m] = r; ++m; }
+    rc = ora_expert_rows(dtype, expert_ptr[e], H, I, x, T, tok, n, o);
+    for (int i = 0; i < n && rc == 0; ++i)
+      memcpy(own_rows + (size_t)pair[i] * H, o + (size_t)i * H, sizeof(double) * (size_t)H);
+    free(tok); free(pair); free(o);
+  }
+  if (rc == 0 && shared) {
+    sh = shared_out ? shared_out : (double*)malloc(sizeof(double) * (size_t)T * H);
+    int32_t* all = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+    for (int t = 0; t < T; ++t) all[t] = t;
+    rc = ora_expert_rows(dtype, shared, H, I_shared, x, T, all, T, sh);
+    free(all);
+  }
+  if (rc == 0) ora_combine(own_rows, w, sh, T, k, H, y);
+  if (!rows) free(own_rows);
+  if (sh && !shared_out) free(sh);
+  return rc;
+}
+
+/* ===========================================================================
+ * Global LRU expert cache
+ *
+ * The pages: during decode "a shared LRU expert cache spanning all MoE layers"
+ * follows the router ("Three mechanisms", semantic-aware caching), and the first
+ * request is served with a cold cache ("Three mechanisms", elastic memory
+ * management).  Readings taken where they are silent:
+ *  - keys are (layer, expert), key = layer*E + expert; the cache starts empty;
+ *  - within one (step, layer) the active experts are accessed hits first, then
+ *    misses, each group in ascending expert id, hit/miss judged against the state
+ *    before the step (so no expert of the step evicts another when they fit);
+ *  - a miss takes the lowest-index free slot, otherwise evicts the least recently
+ *    used key;
+ *  - when the active set exceeds the capacity S, the accesses run in consecutive
+ *    waves of S.
+ * ======================================================================== */
+
+struct ora_lru {
+  int S, L, E;
+  int64_t clock;
+  int64_t* key_of_slot;  /* [S] */
+  int64_t* tick_of_slot; /* [S] */
+  int32_t* slot_of_key;  /* [L*E], -1 if not resident */
+  char* seen;            /* [L*E] */
+};
+
+ora_lru* ora_lru_new(int n_slots, int n_layers, int n_experts) {
+  if (n_slots <= 0 || n_layers <= 0 || n_experts <= 0) return NULL;
+  ora_lru* c = (ora_lru*)calloc(1, sizeof *c);
+  size_t nk = (size_t)n_layers * (size_t)n_experts;
+  c->S = n_slots; c->L = n_layers; c->E = n_experts; c->clock = 0;
+  c->key_of_slot = (int64_t*)malloc(sizeof(int64_t) * (size_t)n_slots);
+  c->tick_of_slot = (int64_t*)malloc(sizeof(int64_t) * (size_t)n_slots);
+  c->slot_of_key = (int32_t*)malloc(sizeof(int32_t) * nk);
+  c->seen = (char*)calloc(nk, 1);
+  for (int s = 0; s < n_slots; ++s) { c->key_of_slot[s] = -1; c->tick_of_slot[s] = -1; }
+  for (size_t q = 0; q < nk; ++q) c->slot_of_key[q] = -1;
+  return c;
+}
+
+void ora_lru_free(ora_lru* c) {
+  if (!c) return;
+  free(c->key_of_slot); free(c->tick_of_slot); free(c->slot_of_key); free(c->seen); free(c);
+}
+
+/* One textbook LRU access.  Returns the slot; *hit, *evicted as outputs. */
+static int lru_access(ora_lru* c, int64_t key, int* hit, int64_t* evicted) {
+  int s = c->slot_of_key[key];
+  *evicted = -1;
+  if (s >= 0) {
+    *hit = 1;
+  } else {
+    *hit = 0;
+    for (int q = 0; q < c->S && s < 0; ++q)
+      if (c->key_of_slot[q] < 0) s = q;
+    if (s < 0) {
+      s = 0;
+      for (int q = 1; q < c->S; ++q)
+        if (c->tick_of_slot[q] < c->tick_of_slot[s]) s = q;
+      *evicted = c->key_of_slot[s];
+      c->slot_of_key[*evicted] = -1;
+    }
+    c->key_of_slot[s] = key;
+    c->slot_of_key[key] = s;
+  }
+  c->tick_of_slot[s] = ++c->clock;
+  return s;
+}
+
+int ora_lru_step(ora_lru* c, int layer, const int32_t* counts, int* n_access, int32_t* acc_expert,
+                 int32_t* acc_hit, int32_t* acc_slot, int32_t* acc_wave, int32_t* acc_cold,
+                 int64_t* acc_evicted) {
+  if (!c || layer < 0 || layer >= c->L) return -1;
+  int n = 0;
+  /* hits first (state before the step), ascending expert id ... */
+  for (int e = 0; e < c->E; ++e)
+    if (counts[e] > 0 && c->slot_of_key[(int64_t)layer * c->E + e] >= 0) acc_expert[n++] = e;
+  /* ... then misses, ascending expert id */
+  for (int e = 0; e < c->E; ++e)
+    if (counts[e] > 0 && c->slot_of_key[(int64_t)layer * c->E + e] < 0) acc_expert[n++] = e;
+  for (int a = 0; a < n; ++a) {
+    int64_t key = (int64_t)layer * c->E + acc_expert[a];
+    int hit;
+    int64_t ev;
+    acc_cold[a] = !c->seen[key];
+    c->seen[key] = 1;
+    acc_slot[a] = lru_access(c, key, &hit, &ev);
+    acc_hit[a] = hit;
+    acc_evicted[a] = ev;
+    acc_wave[a] = a / c->S;
+  }
+  *n_access = n;
+  return n == 0 ? 0 : (n - 1) / c->S + 1;
+}
+
+void ora_lru_state(const ora_lru* c, int64_t* key_of_slot, int64_t* tick_of_slot) {
+  for (int s = 0; s < c->S; ++s) {
+    key_of_slot[s] = c->key_of_slot[s];
+    tick_of_slot[s] = c->tick_of_slot[s];
+  }
+}
