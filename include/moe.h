@@ -1,0 +1,249 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed-expert MoE layer library, libmoe.so.
+ *
+ * One MoE layer's routed-expert forward pass, as the hot path of the edge MoE
+ * serving engine described in "Meet FreeToken: An Edge-Native MoE Serving Engine
+ * that Runs 753B GLM-5.2 on a Single Workstation GPU" (MarkTechPost):
+ *
+ *   moe_route_topk         top-k gating over router logits
+ *   moe_permute            stable permutation of (token, choice) pairs by expert
+ *   moe_cache_lookup_fill  global-LRU expert-slot cache in HBM, filled from pinned host memory
+ *   moe_grouped_ffn        grouped SwiGLU expert FFN (f32, bf16 or MXFP4 weights)
+ *   moe_combine            gate-weighted merge of the expert outputs
+ *   moe_layer_stream_*     whole-layer double buffering for prefill
+ *
+ * Conventions
+ *  - Pointers are device pointers unless the name ends in _host.
+ *  - Every call returns a moe_status; nothing throws, aborts or exits.  On failure
+ *    moe_last_error() holds a message for the calling thread.
+ *  - Calls that take a hipStream_t are asynchronous on it, except
+ *    moe_cache_lookup_fill for wave 0 (it waits for the step's expert counts).
+ *  - The caller owns every buffer and stream.  The library owns only the opaque
+ *    handles (host metadata and HIP events) and allocates no device memory on the
+ *    hot path: scratch comes from the caller through moe_grouped_ffn_workspace().
+ *  - Device buffers must be 16-byte aligned.
+ *  - Shapes: 1 <= E <= 1024, 1 <= k <= min(E, 32), T >= 0, T*k < 2^31,
+ *    H and I multiples of 32 for bf16/MXFP4 weights (multiples of 4 for f32).
+ *  - Logits must be finite; a NaN logit makes the selection unspecified.
+ *
+ * Expert slot layout (one expert = one contiguous run of moe_expert_bytes(); the
+ * host pool stores experts in this final layout so that a fill is one copy):
+ *    f32 / bf16 :  W13 [2I][H] then W2 [H][I], rows K-contiguous
+ *    MXFP4      :  W13 codes [2I][H/2], W2 codes [H][I/2],
+ *                  W13 scales [2I][H/32], W2 scales [H][I/32]
+ *  Rows 0..I-1 of W13 are the gate projection, rows I..2I-1 the up projection,
+ *  W2 is the down projection.  MXFP4 follows OCP MX v1.0: E2M1 elements, one E8M0
+ *  scale per 32 consecutive elements of a row, element 2i in the low nibble.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,         /* bad argument (shape, null or misaligned pointer, range) */
+  MOE_EUNSUPPORTED = 2,   /* valid request this build does not implement */
+  MOE_ECAPACITY = 3,      /* workspace or buffer too small */
+  MOE_EHIP = 4,           /* a HIP runtime call or kernel launch failed */
+  MOE_ENOMEM = 5,         /* host allocation failed */
+  MOE_ESTATE = 6          /* call out of order (e.g. wave w before wave w-1) */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
+
+int moe_abi_version(void);
+const char* moe_status_str(int status);
+const char* moe_last_error(void);
+
+/* Bytes of one expert slot of the given weight type (0 for invalid shapes). */
+size_t moe_expert_bytes(int wdt, int H, int I);
+
+/* ------------------------------------------------------------------------- */
+/* Top-k gating.  The pages: the engine follows the router and never modifies
+ * it ("Three mechanisms": bandwidth-adaptive execution; "Key Takeaways").
+ * For each token t: the k experts with the largest f32 logits, in descending
+ * logit order, equal logits (IEEE equality, -0.0 == +0.0) going to the lower
+ * expert index; gate weights are the softmax over the k selected logits (equal,
+ * in exact arithmetic, to softmax over all E renormalised over the selection),
+ * computed in f32.
+ *   logits   [T][E] f32          (read)
+ *   topk_ids [T][k] int32        (written)  expert ids, bit-exact
+ *   topk_w   [T][k] f32          (written)  gate weights, sum to 1 within rounding */
+int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Permutation by expert (the grouping step between routing and the grouped FFN;
+ * the pages route each token to its experts, "The gap it targets").  Stable
+ * counting sort of the pairs r = t*k + j by topk_ids[r]:
+ *   counts      [E]    pairs per expert
+ *   offsets     [E+1]  exclusive prefix sum, offsets[E] = T*k
+ *   sorted_rows [T*k]  r grouped by expert, ascending r within an expert
+ *   inv_rows    [T*k]  position of r in sorted_rows
+ * Deterministic, bit-exact.  topk_ids values must lie in [0, E). */
+int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                int32_t* sorted_rows, int32_t* inv_rows, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Expert-slot cache.  The pages: inactive experts sit in host memory and enter
+ * the execution path on demand ("The gap it targets"); during decode a shared
+ * LRU expert cache spanning all MoE layers follows the router ("Three
+ * mechanisms": semantic-aware caching); experts are pinned in their final host
+ * layout and the first request starts from a cold cache ("Three mechanisms":
+ * elastic memory management).
+ *
+ * Keys are (layer, expert), key = layer*n_experts + expert.  The cache starts
+ * empty.  For one (step, layer) the active experts (counts > 0) are accessed
+ * hits first, then misses, each group in ascending expert id, hit or miss judged
+ * against the state before the step; a miss takes the lowest-index free slot,
+ * else evicts the least recently used key.  If more experts are active than
+ * there are slots, the accesses run in waves of n_slots: the caller runs the FFN
+ * of wave w before asking for wave w+1.  The shared expert is never cached. */
+typedef struct moe_cache moe_cache;
+
+typedef struct {
+  int n_layers;
+  int n_experts;
+  int n_slots;
+  size_t expert_bytes;  /* bytes copied per fill */
+  size_t slot_stride;   /* bytes between slots in slot_pool; >= expert_bytes, multiple of 256 */
+  void* slot_pool;      /* device, n_slots*slot_stride bytes; NULL = host-only planning handle */
+  const void* host_pool_host;               /* pinned, key-major, expert_bytes per key */
+  const void* const* host_expert_ptrs_host; /* optional [n_layers*n_experts] pinned pointers; overrides host_pool_host */
+  hipStream_t fill_stream;                  /* side stream the fills run on (device handles) */
+} moe_cache_desc;
+
+typedef struct {
+  int64_t accesses;     /* distinct active experts of the step (all waves) */
+  int64_t hits;
+  int64_t misses;
+  int64_t cold_misses;  /* misses of keys never accessed before */
+  int64_t fill_bytes;   /* bytes copied by this call */
+  int32_t n_waves;      /* waves this step needs */
+  int32_t wave_accesses;/* accesses in the wave this call handled */
+} moe_cache_stats;
+
+typedef struct {
+  int32_t slot;
+  int32_t layer;
+  int32_t expert;
+  int32_t wave;
+} moe_fill;
+
+int moe_cache_create(const moe_cache_desc* desc, moe_cache** out);
+/* Waits for the handle's in-flight fills, then frees it. */
+int moe_cache_destroy(moe_cache* c);
+
+/* Device handle.  counts: device [n_experts] (moe_permute output).  For wave 0
+ * the counts are copied to the host and the call waits for them (the only host
+ * synchronisation of the layer); waves 1.. must follow in order, each after the
+ * FFN of the previous wave has been enqueued on compute_stream.  Writes
+ * slot_of_expert (device [n_experts]): the slot of each expert in this wave, -1
+ * for the rest.  Fills run on the fill stream after all work enqueued on
+ * compute_stream so far (write-after-read on victim slots); compute_stream then
+ * waits for them (read-after-write).  stats_host (nullable) receives the
+ * counters.  On error no key maps to a slot whose bytes may have been
+ * overwritten; the rest of the state is as before the call. */
+int moe_cache_lookup_fill(moe_cache* c, int layer, const int32_t* counts, int wave,
+                          int32_t* slot_of_expert, moe_cache_stats* stats_host, hipStream_t compute_stream);
+
+/* Same policy without any device work: counts_host in, slot table and the list
+ * of fills (slot, layer, expert, wave) out, for the caller to perform.  Works on
+ * host-only and device handles.  max_fills >= n_slots is always enough. */
+int moe_cache_lookup_host(moe_cache* c, int layer, const int32_t* counts_host, int wave,
+                          int32_t* slot_of_expert_host, moe_fill* fills_host, int max_fills,
+                          int* n_fills_host, moe_cache_stats* stats_host);
+
+/* Snapshot: key held by each slot (-1 if empty) and its last-use tick. */
+int moe_cache_state(const moe_cache* c, int64_t* key_of_slot_host, int64_t* tick_of_slot_host);
+
+/* Test hook for failure handling: make the (n+1)-th fill from now fail with
+ * MOE_EHIP without issuing it (n < 0 disables). */
+int moe_cache_inject_fill_failure(moe_cache* c, int64_t n);
+
+/* ------------------------------------------------------------------------- */
+/* Grouped SwiGLU expert FFN.  The pages: GPU expert compute on cached and filled
+ * experts, bit-exact with no precision relaxation ("Three mechanisms";
+ * "Key Takeaways").  For every expert e with counts > 0 and slot_of_expert[e] >= 0,
+ * for each of its pairs p in [offsets[e], offsets[e+1]) with token t = sorted_rows[p]/k:
+ *     out_rows[p] = W2 . ( SiLU(Wgate . x[t]) * (Wup . x[t]) ),   SiLU(z) = z/(1+e^-z)
+ * with the expert's weights at slot_pool + slot*slot_stride.  Rows of experts
+ * without a slot are not written.  If shared_w is non-null, the shared expert
+ * (intermediate I_shared, same layout, always resident) is applied to every
+ * token: shared_out[t] = FFN_shared(x[t]).
+ *   wdt         weight type (moe_dtype)
+ *   x           [T][H] f32 for MOE_F32, bf16 otherwise
+ *   out_rows    [T*k][H] f32, indexed by sorted position
+ *   shared_out  [T][H] f32 (required iff shared_w)
+ *   workspace   >= moe_grouped_ffn_workspace() bytes of device memory
+ * Arithmetic: f32 weights use f32 FMA; bf16 and MXFP4 weights use bf16 MFMA
+ * with f32 accumulation (MXFP4 is expanded to bf16 exactly), and the SwiGLU
+ * intermediate is rounded to bf16. */
+size_t moe_grouped_ffn_workspace(int T, int k, int E, int H, int I, int I_shared, int wdt);
+int moe_grouped_ffn(int wdt, const void* slot_pool, size_t slot_stride, const int32_t* slot_of_expert,
+                    const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
+                    const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
+                    float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream);
+/* The two phases of moe_grouped_ffn, same arguments: gate_up writes the SwiGLU
+ * intermediate into the workspace, down reads it.  moe_grouped_ffn is exactly
+ * gate_up followed by down on the same stream. */
+int moe_grouped_ffn_gate_up(int wdt, const void* slot_pool, size_t slot_stride, const int32_t* slot_of_expert,
+                            const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
+                            const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
+                            float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream);
+int moe_grouped_ffn_down(int wdt, const void* slot_pool, size_t slot_stride, const int32_t* slot_of_expert,
+                         const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
+                         const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
+                         float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Combine.  The pages: the partial sums merge exactly ("Three mechanisms").
+ *   y[t] = sum_{j=0..k-1} topk_w[t][j] * out_rows[inv_rows[t*k+j]]  (+ shared_out[t])
+ * in f32, j in increasing order (fused multiply-add), then the shared term,
+ * then one rounding to ydt (MOE_F32, or MOE_BF16 with round-to-nearest-even).
+ * The fixed order makes the result independent of how experts were split into
+ * cache waves.  y: [T][H] of ydt. */
+int moe_combine(const float* out_rows, const float* topk_w, const int32_t* inv_rows, const float* shared_out,
+                int T, int k, int H, void* y, int ydt, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Whole-layer streaming for prefill.  The pages: during prefill, full-layer
+ * double buffering streams layer l+1 while the GPU computes layer l ("Three
+ * mechanisms": semantic-aware caching).  Two device banks each hold one layer
+ * (layer_bytes); a fill copies one layer from pinned host memory with one
+ * hipMemcpyAsync on the fill stream.  Ordering: fill(bank) waits for the last
+ * release(bank); acquire(bank) makes the compute stream wait for the last
+ * fill(bank); release(bank) marks the compute work enqueued so far as the last
+ * reader of the bank.  Typical loop: fill(0, b0); for l: fill(l+1, b(l+1));
+ * acquire(b(l)); compute(l); release(b(l)). */
+typedef struct moe_layer_stream moe_layer_stream;
+
+typedef struct {
+  int n_layers;
+  size_t layer_bytes;
+  const void* host_layers_host;            /* pinned [n_layers][layer_bytes] */
+  const void* const* host_layer_ptrs_host; /* optional [n_layers] pinned pointers; overrides host_layers_host */
+  void* banks[2];                          /* device, layer_bytes each */
+  hipStream_t fill_stream;
+} moe_layer_stream_desc;
+
+int moe_layer_stream_create(const moe_layer_stream_desc* desc, moe_layer_stream** out);
+int moe_layer_stream_destroy(moe_layer_stream* s);
+int moe_layer_stream_fill(moe_layer_stream* s, int layer, int bank);
+int moe_layer_stream_acquire(moe_layer_stream* s, int bank, hipStream_t compute_stream);
+int moe_layer_stream_release(moe_layer_stream* s, int bank, hipStream_t compute_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,560 @@
+// api.cpp -- the C ABI of libmoe (declared in include/moe.h): argument checks,
+// error reporting, kernel dispatch, the device side of the expert-slot cache
+// (fills on a side stream fenced by events) and the prefill layer streamer.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "cache_core.hpp"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE(cond, ...)                          \
+  do {                                              \
+    if (!(cond)) return fail(MOE_EINVAL, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p)                                                              \
+  do {                                                                              \
+    if ((p) == nullptr) return fail(MOE_EINVAL, "%s must not be null", #p);         \
+    if (!aligned16(p)) return fail(MOE_EINVAL, "%s must be 16-byte aligned", #p);   \
+  } while (0)
+
+int check_dims(int wdt, int H, int I, const char* what) {
+  if (wdt < MOE_F32 || wdt > MOE_MXFP4) return fail(MOE_EINVAL, "%s: unknown weight type %d", what, wdt);
+  if (H <= 0 || I <= 0) return fail(MOE_EINVAL, "%s: H=%d and I=%d must be positive", what, H, I);
+  const int q = wdt == MOE_F32 ? 4 : 32;
+  if (H % q || I % q) return fail(MOE_EINVAL, "%s: H=%d and I=%d must be multiples of %d", what, H, I, q);
+  return MOE_OK;
+}
+
+int check_routing(int T, int E, int k) {
+  if (T < 0) return fail(MOE_EINVAL, "T=%d must be >= 0", T);
+  if (E < 1 || E > 1024) return fail(MOE_EINVAL, "E=%d must be in [1, 1024]", E);
+  if (k < 1 || k > 32 || k > E) return fail(MOE_EINVAL, "k=%d must be in [1, min(E, 32)]", k);
+  if ((int64_t)T * k >= ((int64_t)1 << 31)) return fail(MOE_EINVAL, "T*k must be < 2^31");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported";
+    case MOE_ECAPACITY: return "capacity";
+    case MOE_EHIP: return "HIP error";
+    case MOE_ENOMEM: return "out of host memory";
+    case MOE_ESTATE: return "call out of order";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_expert_bytes(int wdt, int H, int I) {
+  if (H <= 0 || I <= 0) return 0;
+  const size_t n = (size_t)3 * H * I;
+  switch (wdt) {
+    case MOE_F32: return 4 * n;
+    case MOE_BF16: return 2 * n;
+    case MOE_MXFP4: return (H % 32 || I % 32) ? 0 : n / 2 + n / 32;
+    default: return 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  if (int rc = check_routing(T, E, k)) return rc;
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(logits);
+  REQUIRE_PTR(topk_ids);
+  REQUIRE_PTR(topk_w);
+  hipError_t e = moe::launch_topk(logits, T, E, k, topk_ids, topk_w, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route_topk launch");
+}
+
+int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                int32_t* sorted_rows, int32_t* inv_rows, hipStream_t stream) {
+  if (int rc = check_routing(T, E, k)) return rc;
+  REQUIRE_PTR(counts);
+  REQUIRE_PTR(offsets);
+  if (T > 0) {
+    REQUIRE_PTR(topk_ids);
+    REQUIRE_PTR(sorted_rows);
+    REQUIRE_PTR(inv_rows);
+  }
+  hipError_t e = moe::launch_permute(topk_ids, T, k, E, counts, offsets, sorted_rows, inv_rows, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_permute launch");
+}
+
+int moe_combine(const float* out_rows, const float* topk_w, const int32_t* inv_rows, const float* shared_out, int T,
+                int k, int H, void* y, int ydt, hipStream_t stream) {
+  if (T < 0 || k < 1 || k > 32 || H <= 0 || H % 4) return fail(MOE_EINVAL, "moe_combine: bad T=%d k=%d H=%d", T, k, H);
+  if (ydt != MOE_F32 && ydt != MOE_BF16) return fail(MOE_EINVAL, "moe_combine: ydt must be MOE_F32 or MOE_BF16");
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(out_rows);
+  REQUIRE_PTR(topk_w);
+  REQUIRE_PTR(inv_rows);
+  REQUIRE_PTR(y);
+  if (shared_out && !aligned16(shared_out)) return fail(MOE_EINVAL, "shared_out must be 16-byte aligned");
+  hipError_t e = moe::launch_combine(out_rows, topk_w, inv_rows, shared_out, T, k, H, y, ydt == MOE_BF16, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_combine launch");
+}
+
+// ---------------------------------------------------------------------------
+size_t moe_grouped_ffn_workspace(int T, int k, int E, int H, int I, int I_shared, int wdt) {
+  (void)E;
+  (void)H;
+  if (T < 0 || k < 1 || I <= 0 || I_shared < 0 || wdt < MOE_F32 || wdt > MOE_MXFP4) return 0;
+  return moe::ffn_workspace_bytes(wdt, T, k, I, I_shared);
+}
+
+namespace {
+
+enum { PHASE_GATE_UP = 1, PHASE_DOWN = 2 };
+
+int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, const int32_t* slot_of_expert,
+                const void* shared_w, int I_shared, const void* x, const int32_t* offsets, const int32_t* sorted_rows,
+                int T, int k, int E, int H, int I, float* out_rows, float* shared_out, void* workspace,
+                size_t ws_bytes, hipStream_t stream) {
+  if (int rc = check_routing(T, E, k)) return rc;
+  if (int rc = check_dims(wdt, H, I, "moe_grouped_ffn")) return rc;
+  if (shared_w) {
+    if (int rc = check_dims(wdt, H, I_shared, "moe_grouped_ffn shared expert")) return rc;
+    REQUIRE_PTR(shared_w);
+    REQUIRE_PTR(shared_out);
+  } else {
+    I_shared = 0;
+  }
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(slot_pool);
+  REQUIRE_PTR(slot_of_expert);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(sorted_rows);
+  REQUIRE_PTR(out_rows);
+  REQUIRE_PTR(workspace);
+  const size_t eb = moe_expert_bytes(wdt, H, I);
+  REQUIRE(slot_stride >= eb && slot_stride % 16 == 0,
+          "slot_stride=%zu must be >= expert bytes %zu and a multiple of 16", slot_stride, eb);
+  const size_t need = moe::ffn_workspace_bytes(wdt, T, k, I, I_shared);
+  if (ws_bytes < need) return fail(MOE_ECAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  moe::FfnArgs a;
+  a.slot_pool = static_cast<const uint8_t*>(slot_pool);
+  a.slot_stride = slot_stride;
+  a.slot_of_expert = slot_of_expert;
+  a.shared_w = static_cast<const uint8_t*>(shared_w);
+  a.x = x;
+  a.offsets = offsets;
+  a.sorted_rows = sorted_rows;
+  a.out_rows = out_rows;
+  a.shared_out = shared_out;
+  a.h = workspace;
+  a.T = T;
+  a.k = k;
+  a.E = E;
+  a.H = H;
+  a.I = I;
+  a.I_shared = I_shared;
+  a.h_ld = I > I_shared ? I : I_shared;
+  a.routed_items = (int)((int64_t)T * k < E ? (int64_t)T * k : E);
+  if (phases & PHASE_GATE_UP) {
+    hipError_t e = moe::launch_ffn_gate_up(wdt, a, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn gate_up launch");
+  }
+  if (phases & PHASE_DOWN) {
+    hipError_t e = moe::launch_ffn_down(wdt, a, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn down launch");
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+int moe_grouped_ffn(int wdt, const void* slot_pool, size_t slot_stride, const int32_t* slot_of_expert,
+                    const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
+                    const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
+                    float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return grouped_ffn(PHASE_GATE_UP | PHASE_DOWN, wdt, slot_pool, slot_stride, slot_of_expert, shared_w, I_shared, x,
+                     offsets, sorted_rows, T, k, E, H, I, out_rows, shared_out, workspace, ws_bytes, stream);
+}
+
+int moe_grouped_ffn_gate_up(int wdt, const void* slot_pool, size_t slot_stride, const int32_t* slot_of_expert,
+                            const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
+                            const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
+                            float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return grouped_ffn(PHASE_GATE_UP, wdt, slot_pool, slot_stride, slot_of_expert, shared_w, I_shared, x, offsets,
+                     sorted_rows, T, k, E, H, I, out_rows, shared_out, workspace, ws_bytes, stream);
+}
+
+int moe_grouped_ffn_down(int wdt, const void* slot_pool, size_t slot_stride, const int32_t* slot_of_expert,
+                         const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
+                         const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
+                         float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return grouped_ffn(PHASE_DOWN, wdt, slot_pool, slot_stride, slot_of_expert, shared_w, I_shared, x, offsets,
+                     sorted_rows, T, k, E, H, I, out_rows, shared_out, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ===========================================================================
+// Expert-slot cache
+// ===========================================================================
+struct moe_cache {
+  moe::LruCore core;
+  moe_cache_desc desc;
+  bool device = false;
+  int32_t* counts_pinned = nullptr;       // [E]
+  int32_t* stage_pinned = nullptr;        // [kStages][E]
+  hipEvent_t stage_ev[8] = {};
+  bool stage_used[8] = {};
+  int stage_next = 0;
+  hipEvent_t ev_counts = nullptr, ev_compute = nullptr, ev_fill = nullptr;
+  int64_t fail_after = -1;                // injected failure: fills left before one fails
+  std::vector<moe::PlannedFill> fills;
+  std::vector<int32_t> table;
+
+  moe_cache(const moe_cache_desc& d) : core(d.n_slots, d.n_layers, d.n_experts), desc(d), table(d.n_experts) {}
+};
+
+namespace {
+constexpr int kStages = 8;
+
+const void* host_src(const moe_cache* c, int layer, int expert) {
+  const int64_t key = (int64_t)layer * c->desc.n_experts + expert;
+  if (c->desc.host_expert_ptrs_host) return c->desc.host_expert_ptrs_host[key];
+  return static_cast<const uint8_t*>(c->desc.host_pool_host) + (size_t)key * c->desc.expert_bytes;
+}
+
+void fill_stats(const moe_cache* c, int nacc, int64_t bytes, moe_cache_stats* st) {
+  if (!st) return;
+  const moe::StepStats& s = c->core.step_stats();
+  st->accesses = s.accesses;
+  st->hits = s.hits;
+  st->misses = s.misses;
+  st->cold_misses = s.cold_misses;
+  st->fill_bytes = bytes;
+  st->n_waves = s.n_waves;
+  st->wave_accesses = nacc;
+}
+
+// Shared between the host and device lookups: open/validate the step and plan the wave.
+int plan(moe_cache* c, int layer, const int32_t* counts_host, int wave, int* nacc) {
+  if (layer < 0 || layer >= c->desc.n_layers) return fail(MOE_EINVAL, "layer %d out of range", layer);
+  if (wave < 0) return fail(MOE_EINVAL, "wave %d < 0", wave);
+  if (wave == 0) {
+    c->core.begin_step(layer, counts_host);
+  } else if (!c->core.step_open() || c->core.next_wave() != wave) {
+    return fail(MOE_ESTATE, "wave %d requested, expected %d", wave,
+                c->core.step_open() ? c->core.next_wave() : 0);
+  }
+  *nacc = c->core.plan_wave(wave, c->table.data(), c->fills);
+  return MOE_OK;
+}
+
+// Returns true if the injected failure fires for the next fill.
+bool injected_failure(moe_cache* c) {
+  if (c->fail_after < 0) return false;
+  if (c->fail_after == 0) {
+    c->fail_after = -1;
+    return true;
+  }
+  --c->fail_after;
+  return false;
+}
+
+void invalidate_upto(moe_cache* c, size_t n_touched) {
+  std::vector<int32_t> slots;
+  for (size_t i = 0; i < n_touched && i < c->fills.size(); ++i) slots.push_back(c->fills[i].slot);
+  c->core.invalidate(slots);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_cache_create(const moe_cache_desc* d, moe_cache** out) {
+  if (!d || !out) return fail(MOE_EINVAL, "moe_cache_create: null argument");
+  *out = nullptr;
+  if (d->n_layers < 1 || d->n_experts < 1 || d->n_experts > 1024 || d->n_slots < 1)
+    return fail(MOE_EINVAL, "moe_cache_create: bad sizes layers=%d experts=%d slots=%d", d->n_layers, d->n_experts,
+                d->n_slots);
+  const bool device = d->slot_pool != nullptr;
+  if (device) {
+    if (d->expert_bytes == 0 || d->slot_stride < d->expert_bytes || d->slot_stride % 256)
+      return fail(MOE_EINVAL, "moe_cache_create: slot_stride must be >= expert_bytes and a multiple of 256");
+    if (((uintptr_t)d->slot_pool & 255u) != 0) return fail(MOE_EINVAL, "slot_pool must be 256-byte aligned");
+    if (!d->host_pool_host && !d->host_expert_ptrs_host)
+      return fail(MOE_EINVAL, "moe_cache_create: a host pool or host pointer table is required");
+  }
+  moe_cache* c = new (std::nothrow) moe_cache(*d);
+  if (!c) return fail(MOE_ENOMEM, "moe_cache_create: out of memory");
+  c->device = device;
+  if (device) {
+    hipError_t e = hipHostMalloc((void**)&c->counts_pinned, sizeof(int32_t) * d->n_experts, hipHostMallocDefault);
+    if (e == hipSuccess)
+      e = hipHostMalloc((void**)&c->stage_pinned, sizeof(int32_t) * d->n_experts * kStages, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_counts, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fill, hipEventDisableTiming);
+    for (int i = 0; i < kStages && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&c->stage_ev[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      moe_cache_destroy(c);
+      return hip_fail(e, "moe_cache_create");
+    }
+  }
+  *out = c;
+  return MOE_OK;
+}
+
+int moe_cache_destroy(moe_cache* c) {
+  if (!c) return MOE_OK;
+  int rc = MOE_OK;
+  if (c->device) {
+    if (c->ev_fill) {
+      hipError_t e = hipEventSynchronize(c->ev_fill);
+      if (e != hipSuccess) rc = hip_fail(e, "moe_cache_destroy: waiting for fills");
+    }
+    for (int i = 0; i < kStages; ++i)
+      if (c->stage_ev[i]) {
+        if (c->stage_used[i]) (void)hipEventSynchronize(c->stage_ev[i]);
+        (void)hipEventDestroy(c->stage_ev[i]);
+      }
+    if (c->ev_counts) (void)hipEventDestroy(c->ev_counts);
+    if (c->ev_compute) (void)hipEventDestroy(c->ev_compute);
+    if (c->ev_fill) (void)hipEventDestroy(c->ev_fill);
+    if (c->counts_pinned) (void)hipHostFree(c->counts_pinned);
+    if (c->stage_pinned) (void)hipHostFree(c->stage_pinned);
+  }
+  delete c;
+  return rc;
+}
+
+int moe_cache_inject_fill_failure(moe_cache* c, int64_t n) {
+  if (!c) return fail(MOE_EINVAL, "null cache");
+  c->fail_after = n < 0 ? -1 : n;
+  return MOE_OK;
+}
+
+int moe_cache_state(const moe_cache* c, int64_t* key_of_slot_host, int64_t* tick_of_slot_host) {
+  if (!c || !key_of_slot_host || !tick_of_slot_host) return fail(MOE_EINVAL, "moe_cache_state: null argument");
+  c->core.state(key_of_slot_host, tick_of_slot_host);
+  return MOE_OK;
+}
+
+int moe_cache_lookup_host(moe_cache* c, int layer, const int32_t* counts_host, int wave, int32_t* slot_of_expert_host,
+                          moe_fill* fills_host, int max_fills, int* n_fills_host, moe_cache_stats* stats_host) {
+  if (!c || !slot_of_expert_host || !n_fills_host) return fail(MOE_EINVAL, "moe_cache_lookup_host: null argument");
+  if (wave == 0 && !counts_host) return fail(MOE_EINVAL, "moe_cache_lookup_host: counts_host is required for wave 0");
+  int nacc = 0;
+  if (int rc = plan(c, layer, counts_host, wave, &nacc)) return rc;
+  if ((int)c->fills.size() > max_fills || (!fills_host && !c->fills.empty())) {
+    c->core.abort_step();
+    return fail(MOE_ECAPACITY, "moe_cache_lookup_host: %zu fills, room for %d", c->fills.size(), max_fills);
+  }
+  for (size_t i = 0; i < c->fills.size(); ++i) {
+    if (injected_failure(c)) {
+      invalidate_upto(c, i + 1);
+      return fail(MOE_EHIP, "moe_cache_lookup_host: injected fill failure at fill %zu", i);
+    }
+  }
+  for (size_t i = 0; i < c->fills.size(); ++i) {
+    fills_host[i].slot = c->fills[i].slot;
+    fills_host[i].layer = layer;
+    fills_host[i].expert = c->fills[i].expert;
+    fills_host[i].wave = wave;
+  }
+  *n_fills_host = (int)c->fills.size();
+  for (int e = 0; e < c->desc.n_experts; ++e) slot_of_expert_host[e] = c->table[e];
+  c->core.commit_wave(wave);
+  fill_stats(c, nacc, (int64_t)c->fills.size() * (int64_t)c->desc.expert_bytes, stats_host);
+  return MOE_OK;
+}
+
+int moe_cache_lookup_fill(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_of_expert,
+                          moe_cache_stats* stats_host, hipStream_t compute_stream) {
+  if (!c) return fail(MOE_EINVAL, "null cache");
+  if (!c->device) return fail(MOE_EINVAL, "moe_cache_lookup_fill needs a device cache (slot_pool set)");
+  REQUIRE_PTR(slot_of_expert);
+  const int E = c->desc.n_experts;
+  hipError_t e;
+  if (wave == 0) {
+    REQUIRE_PTR(counts);
+    // The one host synchronisation of the layer: the step's counts.
+    e = hipMemcpyAsync(c->counts_pinned, counts, sizeof(int32_t) * E, hipMemcpyDeviceToHost, compute_stream);
+    if (e == hipSuccess) e = hipEventRecord(c->ev_counts, compute_stream);
+    if (e == hipSuccess) e = hipEventSynchronize(c->ev_counts);
+    if (e != hipSuccess) return hip_fail(e, "moe_cache_lookup_fill: reading counts");
+  }
+  int nacc = 0;
+  if (int rc = plan(c, layer, c->counts_pinned, wave, &nacc)) return rc;
+  int64_t bytes = 0;
+  if (!c->fills.empty()) {
+    // write-after-read: victims may still be read by FFN work already enqueued
+    e = hipEventRecord(c->ev_compute, compute_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(c->desc.fill_stream, c->ev_compute, 0);
+    if (e != hipSuccess) {
+      c->core.abort_step();
+      return hip_fail(e, "moe_cache_lookup_fill: fencing fills");
+    }
+    for (size_t i = 0; i < c->fills.size(); ++i) {
+      const moe::PlannedFill& f = c->fills[i];
+      if (injected_failure(c)) {
+        invalidate_upto(c, i + 1);
+        return fail(MOE_EHIP, "moe_cache_lookup_fill: injected fill failure at fill %zu", i);
+      }
+      void* dst = static_cast<uint8_t*>(c->desc.slot_pool) + (size_t)f.slot * c->desc.slot_stride;
+      e = hipMemcpyAsync(dst, host_src(c, layer, f.expert), c->desc.expert_bytes, hipMemcpyHostToDevice,
+                         c->desc.fill_stream);
+      if (e != hipSuccess) {
+        invalidate_upto(c, i + 1);
+        return hip_fail(e, "moe_cache_lookup_fill: fill copy");
+      }
+      bytes += (int64_t)c->desc.expert_bytes;
+    }
+    // read-after-write: the FFN of this wave waits for its fills
+    e = hipEventRecord(c->ev_fill, c->desc.fill_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(compute_stream, c->ev_fill, 0);
+    if (e != hipSuccess) {
+      invalidate_upto(c, c->fills.size());
+      return hip_fail(e, "moe_cache_lookup_fill: fencing compute");
+    }
+  }
+  c->core.commit_wave(wave);
+  // slot table upload through a ring of pinned staging buffers
+  const int q = c->stage_next;
+  c->stage_next = (q + 1) % kStages;
+  if (c->stage_used[q]) {
+    e = hipEventSynchronize(c->stage_ev[q]);
+    if (e != hipSuccess) return hip_fail(e, "moe_cache_lookup_fill: staging buffer");
+  }
+  int32_t* stage = c->stage_pinned + (size_t)q * E;
+  for (int x = 0; x < E; ++x) stage[x] = c->table[x];
+  e = hipMemcpyAsync(slot_of_expert, stage, sizeof(int32_t) * E, hipMemcpyHostToDevice, compute_stream);
+  if (e == hipSuccess) e = hipEventRecord(c->stage_ev[q], compute_stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_cache_lookup_fill: slot table upload");
+  c->stage_used[q] = true;
+  fill_stats(c, nacc, bytes, stats_host);
+  return MOE_OK;
+}
+
+}  // extern "C"
+
+// ===========================================================================
+// Prefill layer streaming (two banks)
+// ===========================================================================
+struct moe_layer_stream {
+  moe_layer_stream_desc desc;
+  hipEvent_t ready[2] = {};    // last fill of the bank
+  hipEvent_t released[2] = {}; // last reader of the bank
+  bool filled[2] = {false, false};
+  bool has_release[2] = {false, false};
+};
+
+extern "C" {
+
+int moe_layer_stream_create(const moe_layer_stream_desc* d, moe_layer_stream** out) {
+  if (!d || !out) return fail(MOE_EINVAL, "moe_layer_stream_create: null argument");
+  *out = nullptr;
+  if (d->n_layers < 1 || d->layer_bytes == 0) return fail(MOE_EINVAL, "moe_layer_stream_create: bad sizes");
+  if (!d->banks[0] || !d->banks[1] || !aligned16(d->banks[0]) || !aligned16(d->banks[1]))
+    return fail(MOE_EINVAL, "moe_layer_stream_create: two 16-byte aligned banks are required");
+  if (!d->host_layers_host && !d->host_layer_ptrs_host)
+    return fail(MOE_EINVAL, "moe_layer_stream_create: host layers are required");
+  moe_layer_stream* s = new (std::nothrow) moe_layer_stream();
+  if (!s) return fail(MOE_ENOMEM, "moe_layer_stream_create: out of memory");
+  s->desc = *d;
+  hipError_t e = hipSuccess;
+  for (int b = 0; b < 2 && e == hipSuccess; ++b) {
+    e = hipEventCreateWithFlags(&s->ready[b], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&s->released[b], hipEventDisableTiming);
+  }
+  if (e != hipSuccess) {
+    moe_layer_stream_destroy(s);
+    return hip_fail(e, "moe_layer_stream_create");
+  }
+  *out = s;
+  return MOE_OK;
+}
+
+int moe_layer_stream_destroy(moe_layer_stream* s) {
+  if (!s) return MOE_OK;
+  int rc = MOE_OK;
+  for (int b = 0; b < 2; ++b) {
+    if (s->ready[b]) {
+      if (s->filled[b]) {
+        hipError_t e = hipEventSynchronize(s->ready[b]);
+        if (e != hipSuccess) rc = hip_fail(e, "moe_layer_stream_destroy");
+      }
+      (void)hipEventDestroy(s->ready[b]);
+    }
+    if (s->released[b]) (void)hipEventDestroy(s->released[b]);
+  }
+  delete s;
+  return rc;
+}
+
+int moe_layer_stream_fill(moe_layer_stream* s, int layer, int bank) {
+  if (!s) return fail(MOE_EINVAL, "null layer stream");
+  if (layer < 0 || layer >= s->desc.n_layers || bank < 0 || bank > 1)
+    return fail(MOE_EINVAL, "moe_layer_stream_fill: layer %d / bank %d out of range", layer, bank);
+  hipError_t e = hipSuccess;
+  if (s->has_release[bank]) e = hipStreamWaitEvent(s->desc.fill_stream, s->released[bank], 0);
+  const void* src = s->desc.host_layer_ptrs_host
+                        ? s->desc.host_layer_ptrs_host[layer]
+                        : static_cast<const uint8_t*>(s->desc.host_layers_host) + (size_t)layer * s->desc.layer_bytes;
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(s->desc.banks[bank], src, s->desc.layer_bytes, hipMemcpyHostToDevice, s->desc.fill_stream);
+  if (e == hipSuccess) e = hipEventRecord(s->ready[bank], s->desc.fill_stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_stream_fill");
+  s->filled[bank] = true;
+  return MOE_OK;
+}
+
+int moe_layer_stream_acquire(moe_layer_stream* s, int bank, hipStream_t compute_stream) {
+  if (!s || bank < 0 || bank > 1) return fail(MOE_EINVAL, "moe_layer_stream_acquire: bad argument");
+  if (!s->filled[bank]) return fail(MOE_ESTATE, "moe_layer_stream_acquire: bank %d was never filled", bank);
+  hipError_t e = hipStreamWaitEvent(compute_stream, s->ready[bank], 0);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_layer_stream_acquire");
+}
+
+int moe_layer_stream_release(moe_layer_stream* s, int bank, hipStream_t compute_stream) {
+  if (!s || bank < 0 || bank > 1) return fail(MOE_EINVAL, "moe_layer_stream_release: bad argument");
+  hipError_t e = hipEventRecord(s->released[bank], compute_stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_stream_release");
+  s->has_release[bank] = true;
+  return MOE_OK;
+}
+
+}  // extern "C"

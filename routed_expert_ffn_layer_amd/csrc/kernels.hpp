@@ -1,0 +1,24 @@
+// kernels.hpp -- host-side launchers of the gfx950 kernels (internal to libmoe).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct FfnArgs;
+
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st);
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_rows, int32_t* inv_rows, hipStream_t st);
+hipError_t launch_combine(const float* rows, const float* w, const int32_t* inv, const float* shared, int T, int k,
+                          int H, void* y, bool bf16_out, hipStream_t st);
+
+// Grouped FFN phases.  wtype: 0 f32, 1 bf16, 2 mxfp4.
+hipError_t launch_ffn_gate_up(int wtype, const FfnArgs& a, hipStream_t st);
+hipError_t launch_ffn_down(int wtype, const FfnArgs& a, hipStream_t st);
+// Workspace bytes (the SwiGLU intermediate for T*k routed + T shared rows).
+size_t ffn_workspace_bytes(int wtype, int T, int k, int I, int I_shared);
+
+}  // namespace moe

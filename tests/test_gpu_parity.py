@@ -1,0 +1,247 @@
+"""GPU parity: every kernel through the C ABI against the fp64 CPU oracle.
+
+Integer outputs (expert ids, permutation, cache state) must be bit-exact; gate
+weights within f32 rounding; layer outputs within max-abs 1e-4 (f32 layers) or
+2e-2 * RMS(oracle output) (bf16 and MXFP4 layers).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import (BF16_REL, F32_ATOL, W_ATOL, W_RTOL, assert_close_abs, assert_close_rel, bf16_to_f64,
+                     check_bf16_output, combine_f32, dev, log, pool_from_experts, run_resident_layer, to_dev)
+from routed_expert_ffn_layer_amd import layer as L
+from routed_expert_ffn_layer_amd import moe
+
+pytestmark = pytest.mark.gpu
+
+
+def _topk_gpu(logits, k):
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev())
+    w = torch.empty((T, k), dtype=torch.float32, device=dev())
+    moe.moe_route_topk(to_dev(logits), k, ids, w)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+def _topk_cases():
+    g = np.random.default_rng(100)
+    yield "tiny", synth.tiny_layer()["logits"], 2
+    for T in (1, 4, 16):
+        yield f"decode_T{T}", synth.normal_logits(1002, T, 256, 0), 8
+    yield "zipf_T64", synth.zipf_noise_logits(1003, 64, 256, 5, 1.1), 6
+    yield "prefill_T4096", synth.normal_logits(1004, 4096, 256, 0), 6
+    yield "ties_int", g.integers(0, 3, size=(300, 256)).astype(np.float32), 8
+    yield "all_equal", np.full((7, 100), 0.5, np.float32), 5
+    yield "signed_zero", np.array([[-0.0, 0.0, -1.0, -0.0] + [-2.0] * 60], np.float32), 3
+    yield "E8_k8", g.standard_normal((33, 8)).astype(np.float32), 8
+    yield "E100_k1", g.standard_normal((65, 100)).astype(np.float32), 1
+    yield "E1024_k32", g.standard_normal((9, 1024)).astype(np.float32), 32
+    yield "E513_k16_ties", g.integers(-2, 2, size=(20, 513)).astype(np.float32), 16
+
+
+@pytest.mark.parametrize("case", list(_topk_cases()), ids=lambda c: c[0])
+def test_topk_matches_oracle(ora, case):
+    name, logits, k = case
+    log(f"topk case {name} T={logits.shape[0]} E={logits.shape[1]} k={k}")
+    ids, w = _topk_gpu(logits, k)
+    rids, _, rw = ora.route_topk(logits, k)
+    np.testing.assert_array_equal(ids, rids)
+    np.testing.assert_allclose(w, rw, rtol=W_RTOL, atol=W_ATOL)
+
+
+@pytest.mark.parametrize("T,k,E", [(0, 4, 16), (1, 8, 256), (16, 8, 256), (32, 2, 8), (4096, 6, 256), (3, 1, 1),
+                                   (1000, 32, 1024), (777, 5, 300)])
+def test_permute_matches_oracle(ora, T, k, E):
+    log(f"permute T={T} k={k} E={E}")
+    g = np.random.default_rng(T + E)
+    ids = (np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+           if T else np.zeros((0, k), np.int32))
+    counts = torch.empty(E, dtype=torch.int32, device=dev())
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev())
+    n = max(T * k, 1)
+    srt = torch.full((n,), -7, dtype=torch.int32, device=dev())
+    inv = torch.full((n,), -7, dtype=torch.int32, device=dev())
+    moe.moe_permute(to_dev(ids), E, counts, offsets, srt, inv)
+    torch.cuda.synchronize()
+    rc, ro, rs, ri = ora.permute(ids, E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), rc)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), ro)
+    np.testing.assert_array_equal(srt.cpu().numpy()[:T * k], rs)
+    np.testing.assert_array_equal(inv.cpu().numpy()[:T * k], ri)
+
+
+def _check_layer(ora, lay, b, rel=None):
+    """Compare ids, weights, permutation, expert rows, shared rows and y with the oracle."""
+    dtype = lay["dtype"]
+    H, I, k = lay["H"], lay["I"], lay["k"]
+    ref = ora.layer(dtype, lay["experts"], lay["x"], lay["logits"], k, H, I, shared=lay.get("shared"),
+                    I_shared=lay.get("I_shared", 0))
+    np.testing.assert_array_equal(b.topk_ids.cpu().numpy(), ref["ids"])
+    np.testing.assert_allclose(b.topk_w.cpu().numpy(), ref["w"], rtol=W_RTOL, atol=W_ATOL)
+    inv = b.inv_rows.cpu().numpy()[: b.T * k]
+    rows = b.out_rows.cpu().numpy().astype(np.float64)[inv]
+    if dtype == synth.F32:
+        assert_close_abs(rows, ref["rows"], F32_ATOL, "expert rows")
+        assert_close_abs(b.y.cpu().numpy(), ref["y"], F32_ATOL, "y")
+    else:
+        assert_close_rel(rows, ref["rows"], rel or BF16_REL, "expert rows")
+        if ref["shared_out"] is not None:
+            assert_close_rel(b.shared_out.cpu().numpy()[: b.T], ref["shared_out"], rel or BF16_REL, "shared rows")
+        check_bf16_output(b, ref["shared_out"] is not None, ref["y"], rel or BF16_REL)
+    return ref
+
+
+def test_tiny_f32_layer(ora):
+    lay = synth.tiny_layer()
+    cfg = lay["cfg"]
+    lay = dict(lay, dtype=synth.F32, H=cfg["H"], I=cfg["I"], k=cfg["k"], shared=None, I_shared=0)
+    log("tiny f32 layer T=32 H=256 I=512 E=8 k=2")
+    b, *_ = run_resident_layer(lay)
+    _check_layer(ora, lay, b)
+
+
+# (dtype, T, H, I, E, k, shared): ragged token counts, several token tiles, more
+# than 128 tokens on one expert (two passes), K not a multiple of the MXFP4 step.
+SMALL = [
+    (synth.BF16, 1, 256, 128, 16, 4, True),
+    (synth.BF16, 5, 256, 128, 16, 4, True),
+    (synth.BF16, 40, 512, 256, 32, 6, True),
+    (synth.BF16, 300, 256, 128, 2, 1, False),
+    (synth.BF16, 70, 128, 64, 4, 4, False),
+    (synth.MXFP4, 8, 512, 256, 8, 3, False),
+    (synth.MXFP4, 3, 160, 96, 8, 2, True),
+    (synth.MXFP4, 33, 256, 128, 16, 6, True),
+    (synth.MXFP4, 200, 128, 64, 2, 1, False),
+    (synth.F32, 9, 64, 32, 5, 2, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{synth.DTYPE_NAMES[c[0]]}_T{c[1]}_H{c[2]}_I{c[3]}_E{c[4]}_k{c[5]}_sh{int(c[6])}")
+def test_small_layers(ora, case):
+    dtype, T, H, I, E, k, shared = case
+    log(f"small layer {case}")
+    I_sh = (I // 2 if dtype == synth.F32 else 32 * max(1, I // 64)) if shared else 0
+    lay = synth.small_layer(dtype, T, H, I, E, k, seed=500 + T, shared=shared, I_shared=I_sh)
+    b, *_ = run_resident_layer(lay)
+    _check_layer(ora, lay, b)
+
+
+def test_decode_bf16_full_shape(ora):
+    """Decode layer, bf16: H=2048, I=512, 256 experts + 1 shared, top-8; T = 1, 4, 16."""
+    c = synth.CONFIGS["decode_bf16"]
+    H, I, E, k = c["H"], c["I"], c["E"], c["k"]
+    pool = synth.torch_bf16_expert_pool(E + 1, H, I, seed=c["seed"], device=dev())
+    experts_host = pool.cpu().numpy()
+    slots = pool[:E]
+    shared = pool[E]
+    stride = pool.shape[1]
+    for T in c["T_list"]:
+        log(f"decode bf16 full T={T}")
+        x = synth.encode_activations(synth.BF16, synth.normal_x(c["seed"], T, H, T))
+        logits = synth.normal_logits(c["seed"], T, E, T)
+        b = L.LayerBuffers(T, E, k, H, I, synth.BF16, I_shared=I)
+        L.forward(b, to_dev(logits), to_dev(x), slots, stride, L.identity_slots(E), shared)
+        torch.cuda.synchronize()
+        lay = dict(dtype=synth.BF16, H=H, I=I, k=k, experts=experts_host[:E], x=x, logits=logits,
+                   shared=experts_host[E], I_shared=I)
+        _check_layer(ora, lay, b)
+
+
+def test_decode_mxfp4_full_shape_sampled(ora):
+    """Decode layer, MXFP4: H=4096, I=2048, 256 experts, top-6, Zipf-skewed logits;
+    T = 1, 8, 64.  Routing and permutation are checked in full, expert outputs and
+    y on a sample of tokens."""
+    c = synth.CONFIGS["decode_mxfp4"]
+    H, I, E, k = c["H"], c["I"], c["E"], c["k"]
+    pool = synth.torch_mxfp4_expert_pool(E, H, I, seed=c["seed"], device=dev())
+    stride = pool.shape[1]
+    for T in c["T_list"]:
+        log(f"decode mxfp4 full T={T}")
+        x = synth.encode_activations(synth.MXFP4, synth.normal_x(c["seed"], T, H, T))
+        logits = synth.zipf_noise_logits(c["seed"], T, E, layer=T % 43, s=c["zipf_s"])
+        b = L.LayerBuffers(T, E, k, H, I, synth.MXFP4)
+        L.forward(b, to_dev(logits), to_dev(x), pool, stride, L.identity_slots(E))
+        torch.cuda.synchronize()
+        ids, _, w64 = ora.route_topk(logits, k)
+        np.testing.assert_array_equal(b.topk_ids.cpu().numpy(), ids)
+        rc, ro, rs, ri = ora.permute(ids, E)
+        np.testing.assert_array_equal(b.sorted_rows.cpu().numpy()[: T * k], rs)
+        sample = sorted(set([0, T - 1] + list(np.random.default_rng(T).choice(T, size=min(T, 3), replace=False))))
+        out_rows = b.out_rows.cpu().numpy().astype(np.float64)
+        y_gpu = combine_f32(b, False)
+        # one oracle pass per distinct expert over its sampled tokens
+        by_expert = {}
+        for t in sample:
+            for j in range(k):
+                by_expert.setdefault(int(ids[t, j]), []).append(t)
+        o_ref = {}
+        for e, toks in by_expert.items():
+            o = ora.expert_rows(synth.MXFP4, pool[e].cpu().numpy(), H, I, x, toks)
+            for t, row in zip(toks, o):
+                o_ref[(t, e)] = row
+        y_ref, y_got, rows_ref, rows_got = [], [], [], []
+        for t in sample:
+            yt = np.zeros(H)
+            for j in range(k):
+                o = o_ref[(t, int(ids[t, j]))]
+                rows_ref.append(o)
+                rows_got.append(out_rows[ri[t * k + j]])
+                yt += w64[t, j] * o
+            y_ref.append(yt)
+            y_got.append(y_gpu[t])
+        assert_close_rel(np.array(rows_got), np.array(rows_ref), BF16_REL, "sampled expert rows")
+        assert_close_rel(np.array(y_got), np.array(y_ref), BF16_REL, "sampled y")
+
+
+def test_deterministic_and_doubling_invariant():
+    """Same inputs -> bitwise-equal output; doubling every down-projection weight
+    (bf16: x2 is exact; MXFP4: every W2 scale +1) doubles y bit for bit."""
+    for dtype in (synth.BF16, synth.MXFP4):
+        log(f"determinism/doubling dtype={dtype}")
+        T, H, I, E, k = 24, 256, 128, 16, 4
+        lay = synth.small_layer(dtype, T, H, I, E, k, seed=31, shared=True, I_shared=128)
+        b1, *_ = run_resident_layer(lay)
+        y1 = b1.y.clone()
+        b2, *_ = run_resident_layer(lay)
+        assert torch.equal(y1.view(torch.int16), b2.y.view(torch.int16))
+        doubled = lay["experts"].copy()
+        sh = lay["shared"].copy()
+        if dtype == synth.BF16:
+            off = 2 * 2 * I * H
+            for arr in (doubled[:, off:], sh[None, off:]):
+                v = arr.view(np.uint16).astype(np.uint32)
+                f = (v << 16).view(np.float32) * 2
+                arr[...] = (f.view(np.uint32) >> 16).astype(np.uint16).view(np.uint8).reshape(arr.shape)
+        else:
+            n = 3 * H * I
+            off = n // 2 + 2 * I * H // 32
+            doubled[:, off:] += 1
+            sh[off:] += 1
+        b3, *_ = run_resident_layer(dict(lay, experts=doubled, shared=sh))
+        y3 = b3.y.float()
+        assert torch.equal(y3, 2 * y1.float())
+
+
+def test_identical_experts_reduce_to_dense_ffn(ora):
+    """All experts identical: y = FFN(x) whatever the routing (gate weights sum to 1)."""
+    T, H, I, E, k = 12, 256, 128, 8, 3
+    lay = synth.small_layer(synth.BF16, T, H, I, E, k, seed=41)
+    lay["experts"] = np.stack([lay["experts"][0]] * E)
+    b, *_ = run_resident_layer(lay)
+    dense = ora.expert_rows(synth.BF16, lay["experts"][0], H, I, lay["x"], list(range(T)))
+    check_bf16_output(b, False, dense, BF16_REL, "dense reduction")
+
+
+def test_empty_batch_and_single_expert():
+    log("T=0 and E=1 layers")
+    b = L.LayerBuffers(0, 8, 2, 64, 32, synth.BF16)
+    pool = torch.zeros((8, moe.moe_expert_bytes(1, 64, 32)), dtype=torch.uint8, device=dev())
+    L.forward(b, torch.empty((0, 8), device=dev()), torch.empty((0, 64), dtype=torch.int16, device=dev()), pool,
+              pool.shape[1], L.identity_slots(8))
+    torch.cuda.synchronize()
+    lay = synth.small_layer(synth.BF16, 20, 64, 32, 1, 1, seed=7)
+    b1, *_ = run_resident_layer(lay)
+    assert torch.all(b1.counts == 20) and torch.all(b1.topk_w == 1.0)
