@@ -28,12 +28,20 @@
  *
  * Expert slot layout (one expert = one contiguous run of moe_expert_bytes(); the
  * host pool stores experts in this final layout so that a fill is one copy):
- *    f32 / bf16 :  W13 [2I][H] then W2 [H][I], rows K-contiguous
- *    MXFP4      :  W13 codes [2I][H/2], W2 codes [H][I/2],
- *                  W13 scales [2I][H/32], W2 scales [H][I/32]
- *  Rows 0..I-1 of W13 are the gate projection, rows I..2I-1 the up projection,
- *  W2 is the down projection.  MXFP4 follows OCP MX v1.0: E2M1 elements, one E8M0
- *  scale per 32 consecutive elements of a row, element 2i in the low nibble.
+ *    f32   :  W13 [2I][H] then W2 [H][I], row-major (rows K-contiguous);
+ *             W13 rows 0..I-1 are the gate projection, I..2I-1 the up projection
+ *    bf16  :  W13 (2I rows, K = H) then W2 (H rows, K = I), both tiled
+ *    MXFP4 :  W13 codes, W2 codes, W13 scales, W2 scales, all tiled
+ *  Tiled matrix (R rows, K columns): tiles of 16 rows x KS columns (KS = 32 for
+ *  bf16, 128 for MXFP4; K rounded up to a multiple of KS with zero padding),
+ *  stored row-tile major then column step; each tile is 64 fragments of 16 bytes
+ *  in the order f = 16*g + row%16 with g = (k % KS) / (KS/4): a bf16 fragment is 8
+ *  consecutive k, an MXFP4 fragment one 32-element block (OCP MX v1.0 E2M1,
+ *  element 2i in the low nibble of byte i) whose E8M0 scale is byte f of the
+ *  tile's 64-byte scale block.  This is the operand order of the bf16 MFMA, so a
+ *  wave reads 1 KB of contiguous memory per load.  For bf16 and MXFP4, stored W13
+ *  row 16t+q is gate row 8t+q for q < 8 and up row 8t+q-8 otherwise.  W2 is the
+ *  down projection.
  */
 #ifndef MOE_H
 #define MOE_H

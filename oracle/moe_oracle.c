@@ -45,65 +45,96 @@ double ora_e8m0_value(uint8_t code) {
   return ldexp(1.0, (int)code - 127);
 }
 
-size_t ora_expert_bytes(int dtype, int H, int I) {
-  size_t n = (size_t)3 * (size_t)H * (size_t)I;
-  switch (dtype) {
-    case ORA_F32: return 4 * n;
-    case ORA_BF16: return 2 * n;
-    case ORA_MXFP4: return n / 2 + n / 32;
-    default: return 0;
-  }
+/* Tiled slot layout (a reading: the pages say only that experts are stored in
+ * their "final host layout", "Three mechanisms", elastic memory management).
+ * A matrix of `rows` rows (a multiple of 16) and K columns is cut into tiles of
+ * 16 rows by KS columns (KS = 32 for bf16, 128 for MXFP4); tiles are stored
+ * row-tile major, then by column step.  Inside a tile the 64 fragments of 16
+ * bytes are ordered by f = 16*g + (row % 16), where g = (k % KS) / (KS / 4) is
+ * the column group: a bf16 fragment is 8 consecutive k, an MXFP4 fragment is
+ * one 32-element block (element 2i in the low nibble of byte i).  An MXFP4 matrix
+ * also has one E8M0 byte per fragment, in the same order.  If K is not a
+ * multiple of 128 the last MXFP4 step is padded with zero fragments. */
+static size_t ksteps(int dtype, int K) { return dtype == ORA_MXFP4 ? (size_t)(K + 127) / 128 : (size_t)K / 32; }
+
+static size_t fragment_index(int dtype, int K, int r, int c) {
+  const int KS = dtype == ORA_MXFP4 ? 128 : 32;
+  const size_t tile = (size_t)(r / 16) * ksteps(dtype, K) + (size_t)(c / KS);
+  const int g = (c % KS) / (KS / 4);
+  return tile * 64 + (size_t)(16 * g + r % 16);
 }
 
-/* Element (r, c) of a rows x K matrix stored at `p` in `dtype`.
- * MXFP4 (a reading: the pages only say "MXFP4"): blocks of 32 along K, element
- * 2i in the low nibble of byte i of the row, scales row-major [rows][K/32] in a
- * separate array `s`. */
+/* Element (r, c) of a rows x K matrix: f32 row-major; bf16 and MXFP4 tiled as
+ * above (MXFP4 scales in the separate array `s`). */
 static double element(int dtype, const uint8_t* p, const uint8_t* s, int K, int r, int c) {
-  size_t idx = (size_t)r * (size_t)K + (size_t)c;
   if (dtype == ORA_F32) {
     float f;
-    memcpy(&f, p + 4 * idx, sizeof f);
+    memcpy(&f, p + 4 * ((size_t)r * (size_t)K + (size_t)c), sizeof f);
     return (double)f;
   }
+  const size_t f = fragment_index(dtype, K, r, c);
   if (dtype == ORA_BF16) {
     uint16_t b;
-    memcpy(&b, p + 2 * idx, sizeof b);
+    memcpy(&b, p + 16 * f + 2 * (size_t)(c % 8), sizeof b);
     return ora_bf16_value(b);
   }
   {
-    uint8_t byte = p[(size_t)r * (size_t)(K / 2) + (size_t)(c / 2)];
-    uint8_t code = (c % 2 == 0) ? (uint8_t)(byte & 0x0Fu) : (uint8_t)(byte >> 4);
-    uint8_t scale = s[(size_t)r * (size_t)(K / 32) + (size_t)(c / 32)];
-    return ora_e2m1_value(code) * ora_e8m0_value(scale);
+    const int e = c % 32; /* element inside its block */
+    const uint8_t byte = p[16 * f + (size_t)(e / 2)];
+    const uint8_t code = (e % 2 == 0) ? (uint8_t)(byte & 0x0Fu) : (uint8_t)(byte >> 4);
+    return ora_e2m1_value(code) * ora_e8m0_value(s[f]);
   }
 }
 
+/* Bytes of one tiled matrix (codes, and for MXFP4 the scales). */
+static size_t matrix_bytes(int dtype, int rows, int K) {
+  if (dtype == ORA_F32) return (size_t)4 * rows * K;
+  if (dtype == ORA_BF16) return (size_t)2 * rows * K;
+  return (size_t)(rows / 16) * ksteps(dtype, K) * 1024;
+}
+static size_t scale_bytes(int rows, int K) { return (size_t)(rows / 16) * ksteps(ORA_MXFP4, K) * 64; }
+
+size_t ora_expert_bytes(int dtype, int H, int I) {
+  if (H <= 0 || I <= 0) return 0;
+  if (dtype == ORA_F32 || dtype == ORA_BF16) return matrix_bytes(dtype, 2 * I, H) + matrix_bytes(dtype, H, I);
+  if (dtype != ORA_MXFP4 || H % 32 || I % 32) return 0;
+  return matrix_bytes(dtype, 2 * I, H) + matrix_bytes(dtype, H, I) + scale_bytes(2 * I, H) + scale_bytes(H, I);
+}
+
 /* Slot layout ("final host layout", one contiguous run per expert):
- *   f32/bf16: W13 [2I][H] then W2 [H][I]
- *   mxfp4:    W13 codes [2I][H/2], W2 codes [H][I/2], W13 scales [2I][H/32], W2 scales [H][I/32]
- * Rows 0..I-1 of W13 are the gate projection, rows I..2I-1 the up projection. */
+ *   W13 (2I rows, K = H) then W2 (H rows, K = I); MXFP4: codes of W13, codes of
+ *   W2, scales of W13, scales of W2.
+ * Row order of W13: f32 keeps gate rows 0..I-1 then up rows; bf16 and MXFP4
+ * interleave per 16-row tile: stored row 16t + q holds gate row 8t + q for
+ * q < 8 and up row 8t + q - 8 otherwise. */
 int ora_decode_expert(int dtype, const uint8_t* slot, int H, int I, double* wg, double* wu, double* wd) {
   const uint8_t *w13, *w2, *s13 = NULL, *s2 = NULL;
   if (H <= 0 || I <= 0) return -1;
-  if (dtype == ORA_F32 || dtype == ORA_BF16) {
-    size_t esz = dtype == ORA_F32 ? 4 : 2;
+  if (dtype == ORA_F32) {
     w13 = slot;
-    w2 = slot + esz * 2 * (size_t)I * (size_t)H;
-  } else if (dtype == ORA_MXFP4) {
-    if (H % 32 || I % 32) return -1;
-    w13 = slot;
-    w2 = w13 + (size_t)I * (size_t)H;         /* 2I rows x H/2 bytes */
-    s13 = w2 + (size_t)H * (size_t)I / 2;      /* H rows x I/2 bytes */
-    s2 = s13 + (size_t)2 * I * (size_t)(H / 32);
+    w2 = slot + matrix_bytes(dtype, 2 * I, H);
+    for (int j = 0; j < I; ++j)
+      for (int h = 0; h < H; ++h) {
+        wg[(size_t)j * H + h] = element(dtype, w13, NULL, H, j, h);
+        wu[(size_t)j * H + h] = element(dtype, w13, NULL, H, I + j, h);
+      }
   } else {
-    return -1;
-  }
-  for (int j = 0; j < I; ++j)
-    for (int h = 0; h < H; ++h) {
-      wg[(size_t)j * H + h] = element(dtype, w13, s13, H, j, h);
-      wu[(size_t)j * H + h] = element(dtype, w13, s13, H, I + j, h);
+    if (H % 32 || I % 32) return -1;
+    if (dtype != ORA_BF16 && dtype != ORA_MXFP4) return -1;
+    w13 = slot;
+    w2 = w13 + matrix_bytes(dtype, 2 * I, H);
+    if (dtype == ORA_MXFP4) {
+      s13 = w2 + matrix_bytes(dtype, H, I);
+      s2 = s13 + scale_bytes(2 * I, H);
     }
+    for (int j = 0; j < I; ++j) {
+      const int gate_row = 16 * (j / 8) + j % 8, up_row = gate_row + 8;
+      for (int h = 0; h < H; ++h) {
+        wg[(size_t)j * H + h] = element(dtype, w13, s13, H, gate_row, h);
+        wu[(size_t)j * H + h] = element(dtype, w13, s13, H, up_row, h);
+      }
+    }
+  }
   for (int h = 0; h < H; ++h)
     for (int j = 0; j < I; ++j) wd[(size_t)h * I + j] = element(dtype, w2, s2, I, h, j);
   return 0;

@@ -84,11 +84,15 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 size_t moe_expert_bytes(int wdt, int H, int I) {
   if (H <= 0 || I <= 0) return 0;
-  const size_t n = (size_t)3 * H * I;
   switch (wdt) {
-    case MOE_F32: return 4 * n;
-    case MOE_BF16: return 2 * n;
-    case MOE_MXFP4: return (H % 32 || I % 32) ? 0 : n / 2 + n / 32;
+    case MOE_F32: return (size_t)4 * 3 * H * I;
+    case MOE_BF16: return (H % 32 || I % 32) ? 0 : (size_t)2 * 3 * H * I;
+    case MOE_MXFP4: {
+      if (H % 32 || I % 32) return 0;
+      // tiled: 1 KB of codes and 64 B of scales per 16-row x 128-column tile, K padded to 128
+      const size_t t13 = (size_t)(2 * I / 16) * ((H + 127) / 128), t2 = (size_t)(H / 16) * ((I + 127) / 128);
+      return (t13 + t2) * (1024 + 64);
+    }
     default: return 0;
   }
 }

@@ -43,6 +43,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
 // E8M0 code -> the f32 multiplier 2^(s-127) (s = 0 is the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(s == 0 ? 0x00400000u : (s << 23));
@@ -52,19 +54,25 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
 // block scale -> 8 bf16 in element order.  The hardware convert is exact for every
 // E8M0 scale (products beyond the bf16 range become inf).
 __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float scale) {
-  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
-  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
-  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
-  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
-  bf16x8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
+  u32x4 v;
+  v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Values the whole wave agrees on, moved to scalar registers so that addresses
+// built from them (buffer descriptors, tile offsets) stay scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const uint8_t* uniform(const uint8_t* p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
@@ -81,25 +89,43 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 // Item resolution for the grouped FFN.  The a-th expert (ascending id) that has
 // pairs and a slot in this call.  Every lane of the wave gets the same answer.
-// Returns -1 if fewer than a+1 experts are active.
-__device__ __forceinline__ int nth_active_expert(const int32_t* __restrict__ offsets,
-                                                 const int32_t* __restrict__ slot_of_expert, int E, int a) {
+// Returns -1 if fewer than a+1 experts are active.  All loads are issued before
+// the scan, so the lookup costs one memory round trip.
+template <int EPL>
+__device__ __forceinline__ int nth_active_expert_t(const int32_t* __restrict__ offsets,
+                                                   const int32_t* __restrict__ slot_of_expert, int E, int a) {
   const int lane = threadIdx.x & 63;
+  int lo[EPL], hi[EPL], sl[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = i * 64 + lane;
+    const bool in = e < E;
+    lo[i] = in ? offsets[e] : 0;
+    hi[i] = in ? offsets[e + 1] : 0;
+    sl[i] = in ? slot_of_expert[e] : -1;
+  }
   int base = 0;
-  for (int e0 = 0; e0 < E; e0 += 64) {
-    const int e = e0 + lane;
-    int act = 0;
-    if (e < E) act = (offsets[e + 1] > offsets[e]) && (slot_of_expert[e] >= 0);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int act = (hi[i] > lo[i]) && (sl[i] >= 0);
     const int incl = wave_incl_scan(act);
     const int total = __shfl(incl, 63, 64);
     if (a < base + total) {
-      // lane whose inclusive count reaches a+1 - base while active
       const uint64_t hit = __ballot(act && (incl == a + 1 - base));
-      return e0 + __builtin_ctzll(hit);
+      return i * 64 + __builtin_ctzll(hit);
     }
     base += total;
   }
   return -1;
+}
+
+__device__ __forceinline__ int nth_active_expert(const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ slot_of_expert, int E, int a) {
+  if (E <= 64) return nth_active_expert_t<1>(offsets, slot_of_expert, E, a);
+  if (E <= 128) return nth_active_expert_t<2>(offsets, slot_of_expert, E, a);
+  if (E <= 256) return nth_active_expert_t<4>(offsets, slot_of_expert, E, a);
+  if (E <= 512) return nth_active_expert_t<8>(offsets, slot_of_expert, E, a);
+  return nth_active_expert_t<16>(offsets, slot_of_expert, E, a);
 }
 
 }  // namespace moe

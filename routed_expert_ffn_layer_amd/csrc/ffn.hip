@@ -21,9 +21,15 @@
 // Lane l supplies A[row l%16][8 values] and B[col l%16][8 values]; any fixed
 // assignment of K indices to the 8-value groups is valid as long as A and B use
 // the same one.  bf16 weights: lane group g = l/16 takes k = kb + 8g .. +7.
-// MXFP4: lane group g loads one whole 32-element block (16 bytes of codes, one
+// MXFP4: lane group g takes one whole 32-element block (16 bytes of codes, one
 // scale) at k = kb + 32g and feeds it to 4 MFMAs, the m-th taking elements
 // 8m .. 8m+7.
+//
+// Weights are stored tiled to match (the slot layout of include/moe.h): every
+// 16-row x 32-column (bf16) or 16-row x 128-column (MXFP4) tile is the 64 lanes'
+// 16-byte A fragments in lane order, tiles row-tile major.  One wave load is
+// therefore 1 KB of contiguous HBM, and a wave streams its row tile front to
+// back.  W13 tiles hold 8 gate rows followed by the same 8 up rows.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -58,13 +64,13 @@ __device__ __forceinline__ Item resolve_item(const FfnArgs& a, int shared_tiles,
   const int item = b / routed_tiles;
   it.tile = b - item * routed_tiles;
   it.shared = false;
-  const int e = nth_active_expert(a.offsets, a.slot_of_expert, a.E, item);
+  const int e = uniform(nth_active_expert(a.offsets, a.slot_of_expert, a.E, item));
   it.valid = e >= 0;
   if (!it.valid) return it;
-  it.w = a.slot_pool + (uint64_t)a.slot_of_expert[e] * a.slot_stride;
+  it.w = uniform(a.slot_pool + (uint64_t)uniform(a.slot_of_expert[e]) * a.slot_stride);
   it.I = a.I;
-  it.p0 = a.offsets[e];
-  it.n = a.offsets[e + 1] - it.p0;
+  it.p0 = uniform(a.offsets[e]);
+  it.n = uniform(a.offsets[e + 1]) - it.p0;
   it.hrow0 = it.p0;
   return it;
 }
@@ -136,193 +142,380 @@ struct KStep {
   static constexpr int value = WT == W_MXFP4 ? 128 : 32;
 };
 
-// A fragments of one k step for weight row `wrow` of a K-wide matrix.
-//   bf16:  a[0] = W[wrow][kb+8g .. +7]
-//   mxfp4: a[m] = W[wrow][kb+32g+8m .. +7], m = 0..3 (zeros past K)
-template <int WT>
-__device__ __forceinline__ void load_a(const uint8_t* codes, const uint8_t* scales, int wrow, int K, int kb, int g,
-                                       bf16x8 (&a)[WT == W_MXFP4 ? 4 : 1]) {
-  if constexpr (WT == W_BF16) {
-    a[0] = as_bf16x8(ldg16(codes + ((size_t)wrow * K + kb + 8 * g) * 2));
-  } else {
-    const int kk = kb + 32 * g;
-    if (kk < K) {
-      const u32x4 q = ldg16(codes + (size_t)wrow * (K / 2) + kk / 2);
-      const float sc = e8m0_to_f32(scales[(size_t)wrow * (K / 32) + kk / 32]);
-      a[0] = fp4x8_to_bf16x8(q[0], sc);
-      a[1] = fp4x8_to_bf16x8(q[1], sc);
-      a[2] = fp4x8_to_bf16x8(q[2], sc);
-      a[3] = fp4x8_to_bf16x8(q[3], sc);
-    } else {
+// k steps whose loads are issued together before any of their MFMAs (bounded by
+// the registers the raw A and B fragments take).
+#ifndef MOE_UNROLL_SCALE
+#define MOE_UNROLL_SCALE 1
+#endif
+// k steps per chunk of loads (bounded by the registers two chunks take).
+template <int WT, int NT, int R>
+struct Unroll {
+  static constexpr int raw = WT == W_MXFP4 ? (4 / (NT * R) > 0 ? 4 / (NT * R) : 1)
+                                           : (8 / (NT * R) > 0 ? 8 / (NT * R) : 1);
+  static constexpr int value = MOE_UNROLL_SCALE * (raw > 4 ? 4 : raw);
+};
+
+// Raw fragments of one chunk of U k steps: R weight rows (A) per step and the
+// NT x NA token fragments (B) they share.
+template <int WT, int NT, int R, int U>
+struct Chunk {
+  static constexpr int NA = WT == W_MXFP4 ? 4 : 1;
+  u32x4 qa[U][R];
+  uint32_t qs[U][R];
+  u32x4 qb[U][NT][NA];
+};
+
+// One tiled weight matrix of an expert, addressed through buffer resources:
+// the uniform part of every address (tile, step) is a scalar offset and the
+// per-lane part (fragment `lane`) a fixed vector offset, so a load costs no
+// vector ALU work.
+struct Mat {
+  __amdgpu_buffer_rsrc_t codes;   // 1 KB per (row tile, column step)
+  __amdgpu_buffer_rsrc_t scales;  // MXFP4: 64 B per (row tile, column step)
+  int nK;                         // column steps
+  int K;                          // columns
+};
+
+// Token rows of the B operand: a buffer, the row stride in elements, and per
+// token column nt this lane's row index.
+struct Rows {
+  __amdgpu_buffer_rsrc_t buf;
+  int ld;
+};
+
+constexpr int kBufferFlags = 0x00020000;  // raw (untyped) 32-bit buffer access
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes < 0x7fffffffull ? bytes : 0x7fffffffull), kBufferFlags);
+}
+
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Issue the loads of the chunk starting at step s.  Tile t of this wave is row
+// tile atile[t] (wave-uniform); this lane's A fragment of step s is fragment
+// `lane` of tile (atile[t], s).  B fragments come from row brow[nt] of `rows`.
+// No load is predicated, so no lane diverges: padding token columns point at a
+// real row (their MFMA columns are never stored) and token tiles nt >= ntl are
+// skipped uniformly.  Without CLAMP the chunk must lie inside the wave's step
+// range and (MXFP4) K must be a multiple of 128; with CLAMP, steps past s1
+// re-read step s1-1 (never computed) and MXFP4 column groups past K (zero codes
+// in the padded tile) re-read the row's last 8 values, so every access stays in
+// its buffer.
+template <int WT, int NT, int R, int U, bool CLAMP>
+__device__ __forceinline__ void load_chunk(Chunk<WT, NT, R, U>& c, const Mat& w, const int (&atile)[R], int s,
+                                           int s1, int g, const Rows& rows, const int (&brow)[NT], int ntl) {
+  constexpr int KS = KStep<WT>::value;
+  constexpr int NA = Chunk<WT, NT, R, U>::NA;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) a[m] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  for (int t = 0; t < R; ++t) {
+    const int tile_step = atile[t] * w.nK + s;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int du = CLAMP ? min(s + u, s1 - 1) - s : u;
+      c.qa[u][t] = bld16(w.codes, lane * 16, (tile_step + du) * 1024);
+      if constexpr (WT == W_MXFP4)
+        c.qs[u][t] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(w.scales, lane, (tile_step + du) * 64, 0);
+      else
+        c.qs[u][t] = 0u;
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (nt < ntl) {
+      const int row_off = brow[nt] * rows.ld * 2;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int m = 0; m < NA; ++m) {
+          if constexpr (CLAMP) {
+            const int su = min(s + u, s1 - 1);
+            const int kk = WT == W_MXFP4 ? min(su * KS + 32 * g + 8 * m, w.K - 8) : su * KS + 8 * g;
+            c.qb[u][nt][m] = bld16(rows.buf, row_off + kk * 2, 0);
+          } else {
+            const int goff = (WT == W_MXFP4 ? 32 * g : 8 * g) * 2;
+            c.qb[u][nt][m] = bld16(rows.buf, row_off + goff, ((s + u) * KS + 8 * m) * 2);
+          }
+        }
+      }
     }
   }
 }
 
-// B fragment m of one k step from a bf16 row `src` (nullptr = padding column).
-template <int WT>
-__device__ __forceinline__ bf16x8 load_b(const uint16_t* src, int K, int kb, int g, int m) {
-  const int kk = WT == W_MXFP4 ? kb + 32 * g + 8 * m : kb + 8 * g;
-  if (src == nullptr || kk >= K) return as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-  return as_bf16x8(ldg16(src + kk));
-}
-
-// Byte offsets inside an expert slot.
-template <int WT>
-__device__ __forceinline__ void w13_ptrs(const uint8_t* slot, int H, int Ie, const uint8_t*& codes,
-                                         const uint8_t*& scales) {
-  codes = slot;
-  scales = WT == W_MXFP4 ? slot + (size_t)3 * Ie * H / 2 : nullptr;
-}
-template <int WT>
-__device__ __forceinline__ void w2_ptrs(const uint8_t* slot, int H, int Ie, const uint8_t*& codes,
-                                        const uint8_t*& scales) {
-  if constexpr (WT == W_MXFP4) {
-    codes = slot + (size_t)Ie * H;
-    scales = slot + (size_t)3 * Ie * H / 2 + (size_t)2 * Ie * (H / 32);
-  } else {
-    codes = slot + (size_t)4 * Ie * H;
-    scales = nullptr;
+template <int WT, int NT, int R, int U>
+__device__ __forceinline__ void compute_chunk(const Chunk<WT, NT, R, U>& c, int s, int s1, int ntl,
+                                              f32x4 (&acc)[R][NT]) {
+  constexpr int NA = Chunk<WT, NT, R, U>::NA;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (s + u < s1) {
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        bf16x8 A[NA];
+        if constexpr (WT == W_BF16) {
+          A[0] = as_bf16x8(c.qa[u][t]);
+        } else {
+          const float sc = e8m0_to_f32(c.qs[u][t]);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) A[m] = fp4x8_to_bf16x8(c.qa[u][t][m], sc);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if (nt < ntl) {
+#pragma unroll
+            for (int m = 0; m < NA; ++m)
+              acc[t][nt] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m], as_bf16x8(c.qb[u][nt][m]), acc[t][nt], 0, 0, 0);
+          }
+        }
+      }
+    }
   }
 }
 
-// gate_up: a block owns 8 intermediate indices j0..j0+7 of one item: one 16-row
-// A tile = gate rows j0..j0+7 stacked on up rows j0..j0+7, so the epilogue pairs
-// lane l (gate) with lane l+32 (up) and writes h = SiLU(gate) * up as bf16.
-template <int WT, int NT>
+// acc[t][nt] += A_t . B[nt] over the column steps [s0, s1) of matrix w, A_t
+// being row tile atile[t] and B[nt] this lane's token row brow[nt] of `rows`.
+// Two chunks of U steps alternate: the loads of chunk c+1 are in flight while
+// chunk c is computed, so a wave keeps between U and 2U steps of weight loads
+// outstanding; each token fragment is loaded once per step and reused by the R
+// weight tiles.
+template <int WT, int NT, int R>
+__device__ __forceinline__ void mfma_rows(const Mat& w, const int (&atile)[R], int s0, int s1, int g,
+                                          const Rows& rows, const int (&brow)[NT], int ntl, f32x4 (&acc)[R][NT]) {
+  constexpr int U = Unroll<WT, NT, R>::value;
+  if (s0 >= s1) return;
+  Chunk<WT, NT, R, U> c0, c1;
+  if ((s1 - s0) % (2 * U) == 0 && (WT != W_MXFP4 || w.K % 128 == 0)) {
+    load_chunk<WT, NT, R, U, false>(c0, w, atile, s0, s1, g, rows, brow, ntl);
+    for (int s = s0; s < s1; s += 2 * U) {
+      load_chunk<WT, NT, R, U, false>(c1, w, atile, s + U, s1, g, rows, brow, ntl);
+      compute_chunk<WT, NT, R, U>(c0, s, s1, ntl, acc);
+      if (s + 2 * U < s1) load_chunk<WT, NT, R, U, false>(c0, w, atile, s + 2 * U, s1, g, rows, brow, ntl);
+      compute_chunk<WT, NT, R, U>(c1, s + U, s1, ntl, acc);
+    }
+    return;
+  }
+  load_chunk<WT, NT, R, U, true>(c0, w, atile, s0, s1, g, rows, brow, ntl);
+  for (int s = s0; s < s1; s += 2 * U) {
+    load_chunk<WT, NT, R, U, true>(c1, w, atile, s + U, s1, g, rows, brow, ntl);
+    compute_chunk<WT, NT, R, U>(c0, s, s1, ntl, acc);
+    load_chunk<WT, NT, R, U, true>(c0, w, atile, s + 2 * U, s1, g, rows, brow, ntl);
+    compute_chunk<WT, NT, R, U>(c1, s + U, s1, ntl, acc);
+  }
+}
+
+// Column steps of a K-wide matrix and byte offsets inside an expert slot.
+template <int WT>
+__device__ __forceinline__ int ksteps(int K) {
+  return WT == W_MXFP4 ? (K + 127) / 128 : K / 32;
+}
+template <int WT>
+__device__ __forceinline__ Mat w13_mat(const uint8_t* slot, int H, int Ie) {
+  const size_t t13 = (size_t)(2 * Ie / 16) * ksteps<WT>(H), t2 = (size_t)(H / 16) * ksteps<WT>(Ie);
+  Mat m;
+  m.codes = make_rsrc(slot, t13 * 1024);
+  m.scales = make_rsrc(WT == W_MXFP4 ? slot + (t13 + t2) * 1024 : slot, WT == W_MXFP4 ? t13 * 64 : 0);
+  m.nK = ksteps<WT>(H);
+  m.K = H;
+  return m;
+}
+template <int WT>
+__device__ __forceinline__ Mat w2_mat(const uint8_t* slot, int H, int Ie) {
+  const size_t t13 = (size_t)(2 * Ie / 16) * ksteps<WT>(H), t2 = (size_t)(H / 16) * ksteps<WT>(Ie);
+  Mat m;
+  m.codes = make_rsrc(slot + t13 * 1024, t2 * 1024);
+  m.scales = make_rsrc(WT == W_MXFP4 ? slot + (t13 + t2) * 1024 + t13 * 64 : slot, WT == W_MXFP4 ? t2 * 64 : 0);
+  m.nK = ksteps<WT>(Ie);
+  m.K = Ie;
+  return m;
+}
+
+// Block shape (both phases): 4 waves.  Each wave owns R row tiles of 16 rows;
+// KW waves split the K range of the same tiles and add their partial accumulators
+// in a fixed order through LDS.  A block therefore covers 16 * R * (4/KW) rows of
+// one item.
+
+// gate_up: row tile t of a wave is 8 intermediate indices j..j+7 of one item: one
+// 16-row A tile = gate rows j..j+7 stacked on up rows j..j+7, so the epilogue
+// pairs lane l (gate) with lane l+32 (up) and writes h = SiLU(gate) * up as bf16.
+template <int WT, int NT, int KW, int R>
 __global__ __launch_bounds__(256) void gate_up_mfma(FfnArgs a, int shared_tiles, int routed_tiles) {
+  constexpr int RT = 4 / KW;
   const Item it = resolve_item(a, shared_tiles, routed_tiles);
   if (!it.valid) return;
-  constexpr int KS = KStep<WT>::value;
-  constexpr int NA = WT == W_MXFP4 ? 4 : 1;
-  __shared__ f32x4 red[3][NT][64];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ f32x4 red[KW > 1 ? 4 : 1][R][NT][64];
+  const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
+  const int rg = wv / KW, kp = wv % KW;
   const int r = lane & 15, g = lane >> 4;
   const int H = a.H, Ie = it.I;
-  const int j0 = it.tile * 8;
-  const int wrow = r < 8 ? j0 + r : Ie + j0 + (r - 8);
-  const int nsteps = (H + KS - 1) / KS;
-  const int s0 = wv * nsteps / 4, s1 = (wv + 1) * nsteps / 4;
-  const uint8_t *codes, *scales;
-  w13_ptrs<WT>(it.w, H, Ie, codes, scales);
-  const uint16_t* xb = reinterpret_cast<const uint16_t*>(a.x);
+  // tiles of this wave: j0 + 8 t, t < R (the last block of an item may hold fewer)
+  const int j0 = (it.tile * RT + rg) * 8 * R;
+  const int ntiles = max(0, min(R, (Ie - j0) / 8));
+  // W13 row tile j0/8 + t holds gate and up rows of j0+8t .. j0+8t+7
+  int atile[R];
+#pragma unroll
+  for (int t = 0; t < R; ++t) atile[t] = j0 / 8 + t;
+  const int nsteps = ksteps<WT>(H);
+  const int s0 = kp * nsteps / KW, s1 = (kp + 1) * nsteps / KW;
+  const Mat w = w13_mat<WT>(it.w, H, Ie);
+  Rows rows;
+  rows.buf = make_rsrc(a.x, (size_t)a.T * H * 2);
+  rows.ld = H;
   uint16_t* h = reinterpret_cast<uint16_t*>(a.h);
   for (int pass = 0; pass < it.n; pass += NT * 16) {
     const int ntl = min(NT, (it.n - pass + 15) / 16);
-    const uint16_t* xrow[NT];
+    int xrow[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int i = pass + nt * 16 + r;
-      xrow[nt] = (nt < ntl && i < it.n) ? xb + (size_t)item_token(a, it, i) * H : nullptr;
+      const int i = min(pass + nt * 16 + r, it.n - 1);  // padding columns re-read a real row
+      xrow[nt] = item_token(a, it, i);
     }
-    f32x4 acc[NT];
+    f32x4 acc[R][NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int s = s0; s < s1; ++s) {
-      const int kb = s * KS;
-      bf16x8 A[NA];
-      load_a<WT>(codes, scales, wrow, H, kb, g, A);
+    for (int t = 0; t < R; ++t)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (nt < ntl) {
+      for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ntiles == R) {
+      mfma_rows<WT, NT, R>(w, atile, s0, s1, g, rows, xrow, ntl, acc);
+    } else if (ntiles > 0) {
+      // ragged last tiles of the item: one tile at a time
+      for (int t = 0; t < ntiles; ++t) {
+        f32x4 one[1][NT];
 #pragma unroll
-          for (int m = 0; m < NA; ++m)
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m], load_b<WT>(xrow[nt], H, kb, g, m), acc[nt], 0, 0, 0);
-        }
+        for (int nt = 0; nt < NT; ++nt) one[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tile1[1] = {j0 / 8 + t};
+        mfma_rows<WT, NT, 1>(w, tile1, s0, s1, g, rows, xrow, ntl, one);
+#pragma unroll
+        for (int tt = 0; tt < R; ++tt)
+          if (tt == t)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[tt][nt] = one[0][nt];
       }
     }
-    if (wv > 0) {
+    if (KW > 1) {
+      if (kp > 0) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) red[wv - 1][nt][lane] = acc[nt];
+        for (int t = 0; t < R; ++t)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) red[wv][t][nt][lane] = acc[t][nt];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (wv == 0) {
+    if (kp == 0) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (nt < ntl) {
-          const f32x4 v = ((acc[nt] + red[0][nt][lane]) + red[1][nt][lane]) + red[2][nt][lane];
-          f32x4 u;
+      for (int t = 0; t < R; ++t) {
+        if (t < ntiles) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) u[q] = __shfl_xor(v[q], 32, 64);
-          const int i = pass + nt * 16 + r;
-          if (g < 2 && i < it.n) {
-            uint2 packed;
-            packed.x = (uint32_t)f32_to_bf16_rne(silu_f32(v[0]) * u[0]) |
-                       ((uint32_t)f32_to_bf16_rne(silu_f32(v[1]) * u[1]) << 16);
-            packed.y = (uint32_t)f32_to_bf16_rne(silu_f32(v[2]) * u[2]) |
-                       ((uint32_t)f32_to_bf16_rne(silu_f32(v[3]) * u[3]) << 16);
-            *reinterpret_cast<uint2*>(h + (size_t)(it.hrow0 + i) * a.h_ld + j0 + g * 4) = packed;
+          for (int nt = 0; nt < NT; ++nt) {
+            if (nt < ntl) {
+              f32x4 v = acc[t][nt];
+#pragma unroll
+              for (int q = 1; q < KW; ++q) v += red[wv + q][t][nt][lane];
+              f32x4 u;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) u[q] = __shfl_xor(v[q], 32, 64);
+              const int i = pass + nt * 16 + r;
+              if (g < 2 && i < it.n) {
+                uint2 packed;
+                packed.x = (uint32_t)f32_to_bf16_rne(silu_f32(v[0]) * u[0]) |
+                           ((uint32_t)f32_to_bf16_rne(silu_f32(v[1]) * u[1]) << 16);
+                packed.y = (uint32_t)f32_to_bf16_rne(silu_f32(v[2]) * u[2]) |
+                           ((uint32_t)f32_to_bf16_rne(silu_f32(v[3]) * u[3]) << 16);
+                *reinterpret_cast<uint2*>(h + (size_t)(it.hrow0 + i) * a.h_ld + j0 + 8 * t + g * 4) = packed;
+              }
+            }
           }
         }
       }
     }
-    __syncthreads();
+    if (KW > 1) __syncthreads();
   }
 }
 
-// down: a block owns 16 output columns (rows of W2) of one item.
-template <int WT, int NT>
+// down: row tile t of a wave is 16 output columns (rows of W2) of one item.
+template <int WT, int NT, int KW, int R>
 __global__ __launch_bounds__(256) void down_mfma(FfnArgs a, int shared_tiles, int routed_tiles) {
+  constexpr int RT = 4 / KW;
   const Item it = resolve_item(a, shared_tiles, routed_tiles);
   if (!it.valid) return;
-  constexpr int KS = KStep<WT>::value;
-  constexpr int NA = WT == W_MXFP4 ? 4 : 1;
-  __shared__ f32x4 red[3][NT][64];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ f32x4 red[KW > 1 ? 4 : 1][R][NT][64];
+  const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
+  const int rg = wv / KW, kp = wv % KW;
   const int r = lane & 15, g = lane >> 4;
   const int H = a.H, Ie = it.I;
-  const int row0 = it.tile * 16;
-  const int nsteps = (Ie + KS - 1) / KS;
-  const int s0 = wv * nsteps / 4, s1 = (wv + 1) * nsteps / 4;
-  const uint8_t *codes, *scales;
-  w2_ptrs<WT>(it.w, H, Ie, codes, scales);
-  const uint16_t* hb = reinterpret_cast<const uint16_t*>(a.h);
+  const int row0 = (it.tile * RT + rg) * 16 * R;
+  const int ntiles = max(0, min(R, (H - row0) / 16));
+  const int nsteps = ksteps<WT>(Ie);
+  const int s0 = kp * nsteps / KW, s1 = (kp + 1) * nsteps / KW;
+  const Mat w = w2_mat<WT>(it.w, H, Ie);
+  Rows rows;
+  rows.buf = make_rsrc(a.h, ((size_t)a.T * a.k + (a.shared_w ? a.T : 0)) * a.h_ld * 2);
+  rows.ld = a.h_ld;
   for (int pass = 0; pass < it.n; pass += NT * 16) {
     const int ntl = min(NT, (it.n - pass + 15) / 16);
-    const uint16_t* hrow[NT];
+    int hrow[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int i = pass + nt * 16 + r;
-      hrow[nt] = (nt < ntl && i < it.n) ? hb + (size_t)(it.hrow0 + i) * a.h_ld : nullptr;
+      const int i = min(pass + nt * 16 + r, it.n - 1);  // padding columns re-read a real row
+      hrow[nt] = it.hrow0 + i;
     }
-    f32x4 acc[NT];
+    f32x4 acc[R][NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int s = s0; s < s1; ++s) {
-      const int kb = s * KS;
-      bf16x8 A[NA];
-      load_a<WT>(codes, scales, row0 + r, Ie, kb, g, A);
+    for (int t = 0; t < R; ++t)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (nt < ntl) {
+      for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ntiles == R) {
+      int atile[R];
 #pragma unroll
-          for (int m = 0; m < NA; ++m)
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m], load_b<WT>(hrow[nt], Ie, kb, g, m), acc[nt], 0, 0, 0);
-        }
+      for (int t = 0; t < R; ++t) atile[t] = row0 / 16 + t;
+      mfma_rows<WT, NT, R>(w, atile, s0, s1, g, rows, hrow, ntl, acc);
+    } else if (ntiles > 0) {
+      for (int t = 0; t < ntiles; ++t) {
+        f32x4 one[1][NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) one[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tile1[1] = {row0 / 16 + t};
+        mfma_rows<WT, NT, 1>(w, tile1, s0, s1, g, rows, hrow, ntl, one);
+#pragma unroll
+        for (int tt = 0; tt < R; ++tt)
+          if (tt == t)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[tt][nt] = one[0][nt];
       }
     }
-    if (wv > 0) {
+    if (KW > 1) {
+      if (kp > 0) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) red[wv - 1][nt][lane] = acc[nt];
+        for (int t = 0; t < R; ++t)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) red[wv][t][nt][lane] = acc[t][nt];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (wv == 0) {
+    if (kp == 0) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (nt < ntl) {
-          const f32x4 v = ((acc[nt] + red[0][nt][lane]) + red[1][nt][lane]) + red[2][nt][lane];
-          const int i = pass + nt * 16 + r;
-          if (i < it.n) {
-            float* dst = it.shared ? a.shared_out + (size_t)i * H : a.out_rows + (size_t)(it.p0 + i) * H;
-            *reinterpret_cast<float4*>(dst + row0 + g * 4) = make_float4(v[0], v[1], v[2], v[3]);
+      for (int t = 0; t < R; ++t) {
+        if (t < ntiles) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            if (nt < ntl) {
+              f32x4 v = acc[t][nt];
+#pragma unroll
+              for (int q = 1; q < KW; ++q) v += red[wv + q][t][nt][lane];
+              const int i = pass + nt * 16 + r;
+              if (i < it.n) {
+                float* dst = it.shared ? a.shared_out + (size_t)i * H : a.out_rows + (size_t)(it.p0 + i) * H;
+                *reinterpret_cast<float4*>(dst + row0 + 16 * t + g * 4) = make_float4(v[0], v[1], v[2], v[3]);
+              }
+            }
           }
         }
       }
     }
-    __syncthreads();
+    if (KW > 1) __syncthreads();
   }
 }
 
@@ -335,13 +528,22 @@ size_t ffn_workspace_bytes(int wtype, int T, int k, int I, int I_shared) {
   return rows * ld * (wtype == W_F32 ? 4 : 2);
 }
 
-template <int WT, int NT>
-static void launch_gu(const FfnArgs& a, hipStream_t st, unsigned grid, int shared_tiles, int routed_tiles) {
-  hipLaunchKernelGGL((gate_up_mfma<WT, NT>), dim3(grid), dim3(256), 0, st, a, shared_tiles, routed_tiles);
+// Block shapes by weight type, phase and batch, from a sweep on the MI355X
+// (decode shapes: bf16 H=2048/I=512, MXFP4 H=4096/I=2048; T = 1 .. 64):
+//   gate_up bf16   T <= 4: KW=4, R=1   else KW=2, R=1
+//   gate_up MXFP4  T <= 16: KW=1, R=2  else KW=1, R=4
+//   down    bf16   KW=1, R=2
+//   down    MXFP4  T <= 16: KW=1, R=2  else KW=1, R=4
+struct Shape {
+  int kw, r;
+};
+static Shape gate_up_shape(int wtype, int T) {
+  if (wtype == W_BF16) return T <= 4 ? Shape{4, 1} : Shape{2, 1};
+  return T <= 16 ? Shape{1, 2} : Shape{1, 4};
 }
-template <int WT, int NT>
-static void launch_dn(const FfnArgs& a, hipStream_t st, unsigned grid, int shared_tiles, int routed_tiles) {
-  hipLaunchKernelGGL((down_mfma<WT, NT>), dim3(grid), dim3(256), 0, st, a, shared_tiles, routed_tiles);
+static Shape down_shape(int wtype, int T) {
+  if (wtype == W_BF16) return Shape{1, 2};
+  return T <= 16 ? Shape{1, 2} : Shape{1, 4};
 }
 
 static int pick_nt(int T) {
@@ -351,22 +553,22 @@ static int pick_nt(int T) {
   return 8;
 }
 
-template <int WT>
-static void dispatch_gu(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int rt) {
+template <int WT, int KW, int R>
+static void gu_nt(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int rt) {
   switch (pick_nt(a.T)) {
-    case 1: launch_gu<WT, 1>(a, st, grid, sh, rt); break;
-    case 2: launch_gu<WT, 2>(a, st, grid, sh, rt); break;
-    case 4: launch_gu<WT, 4>(a, st, grid, sh, rt); break;
-    default: launch_gu<WT, 8>(a, st, grid, sh, rt); break;
+    case 1: hipLaunchKernelGGL((gate_up_mfma<WT, 1, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
+    case 2: hipLaunchKernelGGL((gate_up_mfma<WT, 2, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
+    case 4: hipLaunchKernelGGL((gate_up_mfma<WT, 4, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
+    default: hipLaunchKernelGGL((gate_up_mfma<WT, 8, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
   }
 }
-template <int WT>
-static void dispatch_dn(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int rt) {
+template <int WT, int KW, int R>
+static void dn_nt(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int rt) {
   switch (pick_nt(a.T)) {
-    case 1: launch_dn<WT, 1>(a, st, grid, sh, rt); break;
-    case 2: launch_dn<WT, 2>(a, st, grid, sh, rt); break;
-    case 4: launch_dn<WT, 4>(a, st, grid, sh, rt); break;
-    default: launch_dn<WT, 8>(a, st, grid, sh, rt); break;
+    case 1: hipLaunchKernelGGL((down_mfma<WT, 1, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
+    case 2: hipLaunchKernelGGL((down_mfma<WT, 2, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
+    case 4: hipLaunchKernelGGL((down_mfma<WT, 4, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
+    default: hipLaunchKernelGGL((down_mfma<WT, 8, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
   }
 }
 
@@ -377,13 +579,19 @@ hipError_t launch_ffn_gate_up(int wtype, const FfnArgs& a, hipStream_t st) {
     const int shared_tiles = sh ? (a.I_shared + 3) / 4 : 0, routed_tiles = (a.I + 3) / 4;
     const unsigned grid = shared_tiles + a.routed_items * routed_tiles;
     if (grid) hipLaunchKernelGGL(gate_up_f32, dim3(grid), dim3(256), 0, st, a, shared_tiles, routed_tiles);
+    return hipGetLastError();
+  }
+  const Shape sp = gate_up_shape(wtype, a.T);
+  const int rb = 8 * sp.r * (4 / sp.kw);  // intermediate indices per block
+  const int shared_tiles = sh ? (a.I_shared + rb - 1) / rb : 0, routed_tiles = (a.I + rb - 1) / rb;
+  const unsigned grid = shared_tiles + a.routed_items * routed_tiles;
+  if (!grid) return hipSuccess;
+  if (wtype == W_BF16) {
+    if (sp.kw == 4) gu_nt<W_BF16, 4, 1>(a, st, grid, shared_tiles, routed_tiles);
+    else gu_nt<W_BF16, 2, 1>(a, st, grid, shared_tiles, routed_tiles);
   } else {
-    const int shared_tiles = sh ? a.I_shared / 8 : 0, routed_tiles = a.I / 8;
-    const unsigned grid = shared_tiles + a.routed_items * routed_tiles;
-    if (grid) {
-      if (wtype == W_BF16) dispatch_gu<W_BF16>(a, st, grid, shared_tiles, routed_tiles);
-      else dispatch_gu<W_MXFP4>(a, st, grid, shared_tiles, routed_tiles);
-    }
+    if (sp.r == 2) gu_nt<W_MXFP4, 1, 2>(a, st, grid, shared_tiles, routed_tiles);
+    else gu_nt<W_MXFP4, 1, 4>(a, st, grid, shared_tiles, routed_tiles);
   }
   return hipGetLastError();
 }
@@ -396,15 +604,17 @@ hipError_t launch_ffn_down(int wtype, const FfnArgs& a, hipStream_t st) {
     const int shared_tiles = sh ? tiles : 0;
     const unsigned grid = shared_tiles + a.routed_items * tiles;
     if (grid) hipLaunchKernelGGL(down_f32, dim3(grid), dim3(256), 0, st, a, shared_tiles, tiles);
-  } else {
-    const int tiles = a.H / 16;
-    const int shared_tiles = sh ? tiles : 0;
-    const unsigned grid = shared_tiles + a.routed_items * tiles;
-    if (grid) {
-      if (wtype == W_BF16) dispatch_dn<W_BF16>(a, st, grid, shared_tiles, tiles);
-      else dispatch_dn<W_MXFP4>(a, st, grid, shared_tiles, tiles);
-    }
+    return hipGetLastError();
   }
+  const Shape sp = down_shape(wtype, a.T);
+  const int rb = 16 * sp.r * (4 / sp.kw);  // output columns per block
+  const int tiles = (a.H + rb - 1) / rb;
+  const int shared_tiles = sh ? tiles : 0;
+  const unsigned grid = shared_tiles + a.routed_items * tiles;
+  if (!grid) return hipSuccess;
+  if (wtype == W_BF16) dn_nt<W_BF16, 1, 2>(a, st, grid, shared_tiles, tiles);
+  else if (sp.r == 2) dn_nt<W_MXFP4, 1, 2>(a, st, grid, shared_tiles, tiles);
+  else dn_nt<W_MXFP4, 1, 4>(a, st, grid, shared_tiles, tiles);
   return hipGetLastError();
 }
 

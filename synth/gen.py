@@ -14,12 +14,19 @@ Formats
 Expert slot layout ("final host layout": one expert is one contiguous run of
 ``expert_bytes`` so a cache fill is a single copy)::
 
-    f32 / bf16 :  W13 [2I][H]  then  W2 [H][I]           (rows K-contiguous)
-    mxfp4      :  W13 codes [2I][H/2], W2 codes [H][I/2],
-                  W13 scales [2I][H/32], W2 scales [H][I/32]
+    f32   :  W13 [2I][H] then W2 [H][I], row-major, rows K-contiguous;
+             W13 rows 0..I-1 gate, I..2I-1 up
+    bf16  :  W13 then W2, each in the tiled layout below
+    mxfp4 :  W13 codes, W2 codes, W13 scales, W2 scales, tiled
 
-Rows 0..I-1 of W13 are the gate projection, rows I..2I-1 the up projection;
-W2 is the down projection.
+Tiled layout of a matrix with R rows (R % 16 == 0) and K columns: tiles of 16
+rows x KS columns (KS = 32 bf16, 128 MXFP4), row-tile major then column step;
+inside a tile, 64 fragments of 16 bytes ordered by f = 16*g + row%16 with
+g = (k % KS) // (KS/4).  A bf16 fragment is 8 consecutive k; an MXFP4 fragment
+is one 32-element block, and its E8M0 scale is byte f of the tile's 64-byte
+scale block.  MXFP4 steps past K are zero padding.  For bf16 and MXFP4 the W13
+rows are interleaved per tile: stored row 16t+q is gate row 8t+q (q < 8) or up
+row 8t+q-8.  W2 is the down projection.
 """
 import numpy as np
 
@@ -88,36 +95,88 @@ def mx_quantize(w) -> tuple:
     return packed, scales
 
 
+def _ksteps(dtype, K):
+    return -(-K // 128) if dtype == MXFP4 else K // 32
+
+
+def _matrix_bytes(dtype, rows, K):
+    if dtype == F32:
+        return 4 * rows * K
+    if dtype == BF16:
+        return 2 * rows * K
+    return rows // 16 * _ksteps(dtype, K) * 1024
+
+
+def _scale_bytes(rows, K):
+    return rows // 16 * _ksteps(MXFP4, K) * 64
+
+
+def slot_offsets(dtype: int, H: int, I: int) -> dict:
+    """Byte offsets of the parts of one expert slot (w13, w2, s13, s2, total)."""
+    o = {"w13": 0, "w2": _matrix_bytes(dtype, 2 * I, H)}
+    end = o["w2"] + _matrix_bytes(dtype, H, I)
+    if dtype == MXFP4:
+        o["s13"] = end
+        o["s2"] = end + _scale_bytes(2 * I, H)
+        end = o["s2"] + _scale_bytes(H, I)
+    o["total"] = end
+    return o
+
+
 def expert_bytes(dtype: int, H: int, I: int) -> int:
     """Bytes of one expert's slot in the documented layout."""
-    n = 3 * H * I
-    if dtype == F32:
-        return 4 * n
-    if dtype == BF16:
-        return 2 * n
     if dtype == MXFP4:
         assert H % 32 == 0 and I % 32 == 0
-        return n // 2 + n // 32
-    raise ValueError(dtype)
+    return slot_offsets(dtype, H, I)["total"]
+
+
+def _tile_bf16(m):
+    R, K = m.shape
+    b = bf16_bits(np.asarray(m, np.float32))
+    return b.reshape(R // 16, 16, K // 32, 4, 8).transpose(0, 2, 3, 1, 4).ravel().view(np.uint8)
+
+
+def _tile_mx(m):
+    R, K = m.shape
+    codes, scales = mx_quantize(m)
+    nk = _ksteps(MXFP4, K)
+    blocks = codes.reshape(R, K // 32, 16)
+    pad_c = np.zeros((R, nk * 4, 16), np.uint8)
+    pad_c[:, : K // 32] = blocks
+    pad_s = np.zeros((R, nk * 4), np.uint8)
+    pad_s[:, : K // 32] = scales
+    tc = pad_c.reshape(R // 16, 16, nk, 4, 16).transpose(0, 2, 3, 1, 4).ravel()
+    ts = pad_s.reshape(R // 16, 16, nk, 4).transpose(0, 2, 3, 1).ravel()
+    return tc, ts
+
+
+def _interleave_w13(w_gate, w_up):
+    I, H = w_gate.shape
+    assert I % 8 == 0
+    w = np.empty((2 * I, H), dtype=np.float64)
+    v = w.reshape(I // 8, 16, H)
+    v[:, :8] = np.asarray(w_gate, np.float64).reshape(I // 8, 8, H)
+    v[:, 8:] = np.asarray(w_up, np.float64).reshape(I // 8, 8, H)
+    return w
 
 
 def pack_expert(dtype: int, w_gate, w_up, w_down) -> np.ndarray:
     """Encode float matrices Wg [I][H], Wu [I][H], Wd [H][I] into one slot (uint8)."""
-    w13 = np.concatenate([np.asarray(w_gate), np.asarray(w_up)], axis=0)
-    w2 = np.asarray(w_down)
+    w_gate, w_up, w_down = (np.asarray(a) for a in (w_gate, w_up, w_down))
+    I, H = w_gate.shape
     if dtype == F32:
-        parts = [w13.astype(np.float32).ravel().view(np.uint8), w2.astype(np.float32).ravel().view(np.uint8)]
+        w13 = np.concatenate([w_gate, w_up], axis=0)
+        parts = [w13.astype(np.float32).ravel().view(np.uint8), w_down.astype(np.float32).ravel().view(np.uint8)]
     elif dtype == BF16:
-        parts = [bf16_bits(w13.astype(np.float32)).ravel().view(np.uint8),
-                 bf16_bits(w2.astype(np.float32)).ravel().view(np.uint8)]
+        w13 = _interleave_w13(w_gate, w_up).astype(np.float32)
+        parts = [_tile_bf16(w13), _tile_bf16(w_down.astype(np.float32))]
     elif dtype == MXFP4:
-        c13, s13 = mx_quantize(w13)
-        c2, s2 = mx_quantize(w2)
-        parts = [c13.ravel(), c2.ravel(), s13.ravel(), s2.ravel()]
+        c13, s13 = _tile_mx(_interleave_w13(w_gate, w_up))
+        c2, s2 = _tile_mx(np.asarray(w_down, np.float64))
+        parts = [c13, c2, s13, s2]
     else:
         raise ValueError(dtype)
     out = np.concatenate(parts).astype(np.uint8)
-    I, H = np.asarray(w_gate).shape
     assert out.size == expert_bytes(dtype, H, I)
     return out
 
@@ -188,11 +247,13 @@ def torch_mx_quantize_flat(w):
 def torch_mxfp4_expert_pool(n_experts: int, H: int, I: int, seed: int, device, std: float = 0.02):
     """uint8 tensor [n_experts][expert_bytes] of MXFP4 experts with N(0, std) weights.
 
-    W13 and W2 rows are K-contiguous and K is a multiple of 32, so the 32-element
-    blocks of each row are consecutive blocks of the flat [W13 | W2] draw vector;
-    codes and scales therefore land in the documented layout directly.
+    Every element is an independent draw, so consecutive 32-element blocks of the
+    flat draw vector can be placed at consecutive fragments of the tiled layout;
+    codes and scales are written in the same fragment order, so each scale sits
+    with its own block.
     """
     import torch
+    assert H % 128 == 0 and I % 128 == 0, "bulk MXFP4 pools need K multiples of 128 (no padding)"
     nb = expert_bytes(MXFP4, H, I)
     n = 3 * H * I
     out = torch.empty((n_experts, nb), dtype=torch.uint8, device=device)

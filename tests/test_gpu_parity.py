@@ -104,7 +104,8 @@ def test_tiny_f32_layer(ora):
 
 
 # (dtype, T, H, I, E, k, shared): ragged token counts, several token tiles, more
-# than 128 tokens on one expert (two passes), K not a multiple of the MXFP4 step.
+# than 128 tokens on one expert (two passes), K not a multiple of the MXFP4 step,
+# row-tile counts that leave a block partly filled.
 SMALL = [
     (synth.BF16, 1, 256, 128, 16, 4, True),
     (synth.BF16, 5, 256, 128, 16, 4, True),
@@ -115,6 +116,8 @@ SMALL = [
     (synth.MXFP4, 3, 160, 96, 8, 2, True),
     (synth.MXFP4, 33, 256, 128, 16, 6, True),
     (synth.MXFP4, 200, 128, 64, 2, 1, False),
+    (synth.MXFP4, 40, 160, 96, 8, 3, True),     # 4-tile down blocks over 10 row tiles: ragged last block
+    (synth.BF16, 20, 160, 96, 8, 3, True),
     (synth.F32, 9, 64, 32, 5, 2, True),
 ]
 
@@ -210,14 +213,13 @@ def test_deterministic_and_doubling_invariant():
         doubled = lay["experts"].copy()
         sh = lay["shared"].copy()
         if dtype == synth.BF16:
-            off = 2 * 2 * I * H
+            off = synth.slot_offsets(dtype, H, I)["w2"]
             for arr in (doubled[:, off:], sh[None, off:]):
                 v = arr.view(np.uint16).astype(np.uint32)
                 f = (v << 16).view(np.float32) * 2
                 arr[...] = (f.view(np.uint32) >> 16).astype(np.uint16).view(np.uint8).reshape(arr.shape)
         else:
-            n = 3 * H * I
-            off = n // 2 + 2 * I * H // 32
+            off = synth.slot_offsets(dtype, H, I)["s2"]
             doubled[:, off:] += 1
             sh[off:] += 1
         b3, *_ = run_resident_layer(dict(lay, experts=doubled, shared=sh))

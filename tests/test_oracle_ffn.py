@@ -108,9 +108,7 @@ def test_mxfp4_scale_increment_doubles_output_exactly(ora):
     T, H, I, E, k = 4, 64, 32, 4, 2
     L, experts, out = _layer(ora, 2, T, H, I, E, k, seed=10)
     bumped = experts.copy()
-    n = 3 * H * I
-    w2_scales = n // 2 + 2 * I * H // 32
-    bumped[:, w2_scales:] += 1
+    bumped[:, synth.slot_offsets(synth.MXFP4, H, I)["s2"]:] += 1
     out2 = ora.layer(2, bumped, L["x"], L["logits"], k, H, I)
     np.testing.assert_array_equal(out2["y"], 2.0 * out["y"])
 

@@ -52,29 +52,40 @@ def test_bf16_widening_matches_numpy(ora):
         assert ora.bf16_value(int(b)) == float(r)
 
 
-def test_mxfp4_slot_layout_hand_built(ora):
-    """A slot assembled byte by byte from the documented layout decodes as intended.
+def _frag(row, k, K, KS):
+    """Fragment index of element (row, k) in the tiled layout, written out from its
+    description: 16-row x KS-column tiles, row-tile major then column step, 64
+    fragments per tile ordered by 16*group + row%16, group = (k%KS)//(KS/4)."""
+    nk = -(-K // KS)
+    return ((row // 16) * nk + k // KS) * 64 + 16 * ((k % KS) // (KS // 4)) + row % 16
 
-    H = I = 32: W13 codes [64][16] bytes, W2 codes [32][16], W13 scales [64][1], W2 scales [32][1].
+
+def test_mxfp4_slot_layout_hand_built(ora):
+    """A slot assembled byte by byte from the layout description decodes as intended.
+
+    H = I = 32: W13 has 64 stored rows (4 tiles x 1 padded step), W2 32 rows (2 tiles);
+    codes 4096 + 2048 bytes, scales 256 + 128 bytes.  Stored W13 row 16t+q is gate
+    row 8t+q for q < 8, up row 8t+q-8 otherwise.
     """
     H = I = 32
     nbytes = ora.expert_bytes(ora.MXFP4, H, I)
-    assert nbytes == 3 * H * I // 2 + 3 * H * I // 32
+    assert nbytes == 4096 + 2048 + 256 + 128
+    c13, c2, s13, s2 = 0, 4096, 6144, 6400
     slot = np.zeros(nbytes, np.uint8)
-    w13_codes = 0
-    w2_codes = 2 * I * H // 2
-    w13_scales = w2_codes + H * I // 2
-    w2_scales = w13_scales + 2 * I * H // 32
-    assert w2_scales + H * I // 32 == nbytes
-    slot[w13_scales:w13_scales + 2 * I] = 127          # scale 1.0 for every W13 row
-    slot[w2_scales:w2_scales + H] = 127
-    slot[w13_codes + 0] = 0x21                          # gate row 0: elem 0 = code 1 (0.5), elem 1 = code 2 (1.0)
-    slot[w13_codes + I * (H // 2) + 3] = 0x9F           # up row 0 (W13 row I), byte 3: elem 6 = code 15 (-6), elem 7 = code 9 (-0.5)
-    slot[w13_scales + I] = 129                          # up row 0 scale 4
-    slot[w2_codes + 5 * (I // 2) + 15] = 0x70           # down row 5, byte 15: elem 30 = 0, elem 31 = code 7 (6)
-    slot[w2_scales + 5] = 126                           # down row 5 scale 0.5
+    slot[s13:s13 + 256] = 127      # scale 1.0 everywhere (padding fragments included)
+    slot[s2:s2 + 128] = 127
+    f = _frag(0, 0, H, 128)          # gate row 0 -> stored row 0; elements 0, 1
+    slot[c13 + 16 * f] = 0x21        # elem 0 = code 1 (0.5), elem 1 = code 2 (1.0)
+    f = _frag(8, 6, H, 128)          # up row 0 -> stored row 8; elements 6, 7 in byte 3
+    slot[c13 + 16 * f + 3] = 0x9F    # elem 6 = code 15 (-6), elem 7 = code 9 (-0.5)
+    slot[s13 + f] = 129              # scale 4
+    f = _frag(16 + 1, 5, H, 128)     # gate row 9 -> stored row 17; element 5 = high nibble of byte 2
+    slot[c13 + 16 * f + 2] = 0x50    # code 5 (3.0)
+    f = _frag(5, 31, I, 128)         # down row 5, element 31 = high nibble of byte 15
+    slot[c2 + 16 * f + 15] = 0x70    # code 7 (6.0)
+    slot[s2 + f] = 126               # scale 0.5
     wg, wu, wd = ora.decode_expert(ora.MXFP4, slot, H, I)
-    exp_g = np.zeros((I, H)); exp_g[0, 0] = 0.5; exp_g[0, 1] = 1.0
+    exp_g = np.zeros((I, H)); exp_g[0, 0] = 0.5; exp_g[0, 1] = 1.0; exp_g[9, 5] = 3.0
     exp_u = np.zeros((I, H)); exp_u[0, 6] = -24.0; exp_u[0, 7] = -2.0
     exp_d = np.zeros((H, I)); exp_d[5, 31] = 3.0
     np.testing.assert_array_equal(wg, exp_g)
@@ -82,18 +93,45 @@ def test_mxfp4_slot_layout_hand_built(ora):
     np.testing.assert_array_equal(wd, exp_d)
 
 
-@pytest.mark.parametrize("dtype", [0, 1])
-def test_dense_slot_layout_hand_built(ora, dtype):
+def test_bf16_slot_layout_hand_built(ora):
+    H, I = 64, 32
+    g = np.random.default_rng(4)
+    wg = g.integers(-50, 50, size=(I, H)).astype(np.float32) / 8   # exactly representable in bf16
+    wu = g.integers(-50, 50, size=(I, H)).astype(np.float32) / 8
+    wd = g.integers(-50, 50, size=(H, I)).astype(np.float32) / 8
+    bits = lambda v: int(np.float32(v).view(np.uint32) >> 16)
+    w13_bytes = 2 * 2 * I * H
+    slot = np.zeros(w13_bytes + 2 * H * I, np.uint8)
+    u16 = slot.view(np.uint16)
+    for j in range(I):
+        for k in range(H):
+            for row, val in ((16 * (j // 8) + j % 8, wg[j, k]), (16 * (j // 8) + 8 + j % 8, wu[j, k])):
+                u16[(16 * _frag(row, k, H, 32)) // 2 + k % 8] = bits(val)
+    for r in range(H):
+        for k in range(I):
+            u16[(w13_bytes + 16 * _frag(r, k, I, 32)) // 2 + k % 8] = bits(wd[r, k])
+    dg, du, dd = ora.decode_expert(ora.BF16, slot, H, I)
+    np.testing.assert_array_equal(dg, wg)
+    np.testing.assert_array_equal(du, wu)
+    np.testing.assert_array_equal(dd, wd)
+    # the generator's packing agrees byte for byte
+    np.testing.assert_array_equal(synth.pack_expert(synth.BF16, wg, wu, wd), slot)
+
+
+def test_f32_slot_layout_hand_built(ora):
     H, I = 4, 2
-    vals = np.arange(3 * H * I, dtype=np.float32) - 7.0  # exactly representable in bf16
-    if dtype == 0:
-        slot = vals.view(np.uint8)
-    else:
-        slot = (vals.view(np.uint32) >> 16).astype(np.uint16).view(np.uint8)
-    wg, wu, wd = ora.decode_expert(dtype, slot, H, I)
+    vals = np.arange(3 * H * I, dtype=np.float32) - 7.0
+    wg, wu, wd = ora.decode_expert(ora.F32, vals.view(np.uint8), H, I)
     np.testing.assert_array_equal(wg, vals[:I * H].reshape(I, H))
     np.testing.assert_array_equal(wu, vals[I * H:2 * I * H].reshape(I, H))
     np.testing.assert_array_equal(wd, vals[2 * I * H:].reshape(H, I))
+
+
+def test_mxfp4_padding_for_k_not_multiple_of_128(ora):
+    H, I = 160, 96   # K = 160 -> 2 steps (96 padded columns); K = 96 -> 1 step (32 padded)
+    nb = ora.expert_bytes(ora.MXFP4, H, I)
+    assert nb == (2 * I // 16) * 2 * 1024 + (H // 16) * 1 * 1024 + (2 * I // 16) * 2 * 64 + (H // 16) * 64
+    assert nb == synth.expert_bytes(synth.MXFP4, H, I)
 
 
 def test_mxfp4_roundtrip_of_representable_values(ora):
