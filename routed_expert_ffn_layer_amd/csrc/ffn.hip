@@ -35,6 +35,11 @@
 
 namespace moe {
 
+template <typename K, typename... Args>
+static void launch_ffn_kernel(K kernel, unsigned grid, hipStream_t st, Args... args) {
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, args...);
+}
+
 struct Item {
   const uint8_t* w;  // expert slot
   int I;             // intermediate size
@@ -556,19 +561,19 @@ static int pick_nt(int T) {
 template <int WT, int KW, int R>
 static void gu_nt(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int rt) {
   switch (pick_nt(a.T)) {
-    case 1: hipLaunchKernelGGL((gate_up_mfma<WT, 1, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
-    case 2: hipLaunchKernelGGL((gate_up_mfma<WT, 2, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
-    case 4: hipLaunchKernelGGL((gate_up_mfma<WT, 4, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
-    default: hipLaunchKernelGGL((gate_up_mfma<WT, 8, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
+    case 1: launch_ffn_kernel(gate_up_mfma<WT, 1, KW, R>, grid, st, a, sh, rt); break;
+    case 2: launch_ffn_kernel(gate_up_mfma<WT, 2, KW, R>, grid, st, a, sh, rt); break;
+    case 4: launch_ffn_kernel(gate_up_mfma<WT, 4, KW, R>, grid, st, a, sh, rt); break;
+    default: launch_ffn_kernel(gate_up_mfma<WT, 8, KW, R>, grid, st, a, sh, rt); break;
   }
 }
 template <int WT, int KW, int R>
 static void dn_nt(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int rt) {
   switch (pick_nt(a.T)) {
-    case 1: hipLaunchKernelGGL((down_mfma<WT, 1, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
-    case 2: hipLaunchKernelGGL((down_mfma<WT, 2, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
-    case 4: hipLaunchKernelGGL((down_mfma<WT, 4, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
-    default: hipLaunchKernelGGL((down_mfma<WT, 8, KW, R>), dim3(grid), dim3(256), 0, st, a, sh, rt); break;
+    case 1: launch_ffn_kernel(down_mfma<WT, 1, KW, R>, grid, st, a, sh, rt); break;
+    case 2: launch_ffn_kernel(down_mfma<WT, 2, KW, R>, grid, st, a, sh, rt); break;
+    case 4: launch_ffn_kernel(down_mfma<WT, 4, KW, R>, grid, st, a, sh, rt); break;
+    default: launch_ffn_kernel(down_mfma<WT, 8, KW, R>, grid, st, a, sh, rt); break;
   }
 }
 
@@ -578,7 +583,7 @@ hipError_t launch_ffn_gate_up(int wtype, const FfnArgs& a, hipStream_t st) {
   if (wtype == W_F32) {
     const int shared_tiles = sh ? (a.I_shared + 3) / 4 : 0, routed_tiles = (a.I + 3) / 4;
     const unsigned grid = shared_tiles + a.routed_items * routed_tiles;
-    if (grid) hipLaunchKernelGGL(gate_up_f32, dim3(grid), dim3(256), 0, st, a, shared_tiles, routed_tiles);
+    if (grid) launch_ffn_kernel(gate_up_f32, grid, st, a, shared_tiles, routed_tiles);
     return hipGetLastError();
   }
   const Shape sp = gate_up_shape(wtype, a.T);
@@ -603,7 +608,7 @@ hipError_t launch_ffn_down(int wtype, const FfnArgs& a, hipStream_t st) {
     const int tiles = (a.H + 3) / 4;
     const int shared_tiles = sh ? tiles : 0;
     const unsigned grid = shared_tiles + a.routed_items * tiles;
-    if (grid) hipLaunchKernelGGL(down_f32, dim3(grid), dim3(256), 0, st, a, shared_tiles, tiles);
+    if (grid) launch_ffn_kernel(down_f32, grid, st, a, shared_tiles, tiles);
     return hipGetLastError();
   }
   const Shape sp = down_shape(wtype, a.T);

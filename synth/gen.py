@@ -202,21 +202,22 @@ def encode_activations(dtype: int, x_f32) -> np.ndarray:
 # Bulk generation on the GPU with torch (large pools).  Same encodings as above.
 # ----------------------------------------------------------------------------
 
-def torch_bf16_expert_pool(n_experts: int, H: int, I: int, seed: int, device, std: float = 0.02):
+def torch_bf16_expert_pool(n_experts: int, H: int, I: int, seed: int, device, std: float = 0.02, chunk: int = 16):
     """uint8 tensor [n_experts][expert_bytes] of bf16 experts with N(0, std) weights.
 
     Every element is an independent draw, so the flat order of the draws does not
     matter for the layout; torch's float32 -> bfloat16 conversion rounds to
-    nearest even.
+    nearest even.  Experts are drawn `chunk` at a time.
     """
     import torch
     nb = expert_bytes(BF16, H, I)
     out = torch.empty((n_experts, nb), dtype=torch.uint8, device=device)
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
-    for e in range(n_experts):
-        w = torch.randn(3 * H * I, generator=g, device=device, dtype=torch.float32) * std
-        out[e].copy_(w.to(torch.bfloat16).view(torch.uint8))
+    for e0 in range(0, n_experts, chunk):
+        e1 = min(n_experts, e0 + chunk)
+        w = torch.randn((e1 - e0, 3 * H * I), generator=g, device=device, dtype=torch.float32) * std
+        out[e0:e1].copy_(w.to(torch.bfloat16).view(torch.uint8))
     return out
 
 
@@ -244,13 +245,13 @@ def torch_mx_quantize_flat(w):
     return packed, (e + 127).to(torch.uint8)
 
 
-def torch_mxfp4_expert_pool(n_experts: int, H: int, I: int, seed: int, device, std: float = 0.02):
+def torch_mxfp4_expert_pool(n_experts: int, H: int, I: int, seed: int, device, std: float = 0.02, chunk: int = 4):
     """uint8 tensor [n_experts][expert_bytes] of MXFP4 experts with N(0, std) weights.
 
     Every element is an independent draw, so consecutive 32-element blocks of the
     flat draw vector can be placed at consecutive fragments of the tiled layout;
     codes and scales are written in the same fragment order, so each scale sits
-    with its own block.
+    with its own block.  Experts are drawn `chunk` at a time.
     """
     import torch
     assert H % 128 == 0 and I % 128 == 0, "bulk MXFP4 pools need K multiples of 128 (no padding)"
@@ -259,9 +260,12 @@ def torch_mxfp4_expert_pool(n_experts: int, H: int, I: int, seed: int, device, s
     out = torch.empty((n_experts, nb), dtype=torch.uint8, device=device)
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
-    for e in range(n_experts):
-        w = torch.randn(n, generator=g, device=device, dtype=torch.float32) * std
+    for e0 in range(0, n_experts, chunk):
+        e1 = min(n_experts, e0 + chunk)
+        w = torch.randn((e1 - e0) * n, generator=g, device=device, dtype=torch.float32) * std
         c, s = torch_mx_quantize_flat(w)
-        out[e, : n // 2].copy_(c)
-        out[e, n // 2:].copy_(s)
+        c = c.view(e1 - e0, n // 2)
+        s = s.view(e1 - e0, n // 32)
+        out[e0:e1, : n // 2].copy_(c)
+        out[e0:e1, n // 2:].copy_(s)
     return out
