@@ -193,12 +193,15 @@ int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, 
   a.I_shared = I_shared;
   a.h_ld = I > I_shared ? I : I_shared;
   a.routed_items = (int)((int64_t)T * k < E ? (int64_t)T * k : E);
+  // Prefill-sized batches (32 or more pairs per expert on average) take the
+  // LDS-staged kernels; the results are the same computation.
+  const bool prefill = (int64_t)T * k >= (int64_t)32 * E && moe::prefill_supported(wdt, H, I, I_shared);
   if (phases & PHASE_GATE_UP) {
-    hipError_t e = moe::launch_ffn_gate_up(wdt, a, stream);
+    hipError_t e = prefill ? moe::launch_prefill_gate_up(wdt, a, stream) : moe::launch_ffn_gate_up(wdt, a, stream);
     if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn gate_up launch");
   }
   if (phases & PHASE_DOWN) {
-    hipError_t e = moe::launch_ffn_down(wdt, a, stream);
+    hipError_t e = prefill ? moe::launch_prefill_down(wdt, a, stream) : moe::launch_ffn_down(wdt, a, stream);
     if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn down launch");
   }
   return MOE_OK;

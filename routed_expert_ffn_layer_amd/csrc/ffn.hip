@@ -30,7 +30,7 @@
 // 16-byte A fragments in lane order, tiles row-tile major.  One wave load is
 // therefore 1 KB of contiguous HBM, and a wave streams its row tile front to
 // back.  W13 tiles hold 8 gate rows followed by the same 8 up rows.
-#include "common.hpp"
+#include "ffn_common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -38,50 +38,6 @@ namespace moe {
 template <typename K, typename... Args>
 static void launch_ffn_kernel(K kernel, unsigned grid, hipStream_t st, Args... args) {
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, args...);
-}
-
-struct Item {
-  const uint8_t* w;  // expert slot
-  int I;             // intermediate size
-  int n;             // tokens of the item
-  int p0;            // first output row (routed: sorted position; shared: 0)
-  int hrow0;         // first row of the item in the intermediate workspace
-  int tile;          // tile index inside the item
-  bool shared;
-  bool valid;
-};
-
-__device__ __forceinline__ Item resolve_item(const FfnArgs& a, int shared_tiles, int routed_tiles) {
-  Item it;
-  int b = blockIdx.x;
-  if (b < shared_tiles) {
-    it.shared = true;
-    it.valid = true;
-    it.w = a.shared_w;
-    it.I = a.I_shared;
-    it.n = a.T;
-    it.p0 = 0;
-    it.hrow0 = a.T * a.k;
-    it.tile = b;
-    return it;
-  }
-  b -= shared_tiles;
-  const int item = b / routed_tiles;
-  it.tile = b - item * routed_tiles;
-  it.shared = false;
-  const int e = uniform(nth_active_expert(a.offsets, a.slot_of_expert, a.E, item));
-  it.valid = e >= 0;
-  if (!it.valid) return it;
-  it.w = uniform(a.slot_pool + (uint64_t)uniform(a.slot_of_expert[e]) * a.slot_stride);
-  it.I = a.I;
-  it.p0 = uniform(a.offsets[e]);
-  it.n = uniform(a.offsets[e + 1]) - it.p0;
-  it.hrow0 = it.p0;
-  return it;
-}
-
-__device__ __forceinline__ int item_token(const FfnArgs& a, const Item& it, int i) {
-  return it.shared ? i : a.sorted_rows[it.p0 + i] / a.k;
 }
 
 // ===========================================================================
@@ -142,13 +98,6 @@ __global__ __launch_bounds__(256) void down_f32(FfnArgs a, int shared_tiles, int
 // ===========================================================================
 // bf16 / MXFP4 weights on bf16 MFMA.
 // ===========================================================================
-template <int WT>
-struct KStep {
-  static constexpr int value = WT == W_MXFP4 ? 128 : 32;
-};
-
-// k steps whose loads are issued together before any of their MFMAs (bounded by
-// the registers the raw A and B fragments take).
 #ifndef MOE_UNROLL_SCALE
 #define MOE_UNROLL_SCALE 1
 #endif
@@ -169,35 +118,6 @@ struct Chunk {
   uint32_t qs[U][R];
   u32x4 qb[U][NT][NA];
 };
-
-// One tiled weight matrix of an expert, addressed through buffer resources:
-// the uniform part of every address (tile, step) is a scalar offset and the
-// per-lane part (fragment `lane`) a fixed vector offset, so a load costs no
-// vector ALU work.
-struct Mat {
-  __amdgpu_buffer_rsrc_t codes;   // 1 KB per (row tile, column step)
-  __amdgpu_buffer_rsrc_t scales;  // MXFP4: 64 B per (row tile, column step)
-  int nK;                         // column steps
-  int K;                          // columns
-};
-
-// Token rows of the B operand: a buffer, the row stride in elements, and per
-// token column nt this lane's row index.
-struct Rows {
-  __amdgpu_buffer_rsrc_t buf;
-  int ld;
-};
-
-constexpr int kBufferFlags = 0x00020000;  // raw (untyped) 32-bit buffer access
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           (int)(bytes < 0x7fffffffull ? bytes : 0x7fffffffull), kBufferFlags);
-}
-
-__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
 
 // Issue the loads of the chunk starting at step s.  Tile t of this wave is row
 // tile atile[t] (wave-uniform); this lane's A fragment of step s is fragment
@@ -310,32 +230,6 @@ __device__ __forceinline__ void mfma_rows(const Mat& w, const int (&atile)[R], i
     load_chunk<WT, NT, R, U, true>(c0, w, atile, s + 2 * U, s1, g, rows, brow, ntl);
     compute_chunk<WT, NT, R, U>(c1, s + U, s1, ntl, acc);
   }
-}
-
-// Column steps of a K-wide matrix and byte offsets inside an expert slot.
-template <int WT>
-__device__ __forceinline__ int ksteps(int K) {
-  return WT == W_MXFP4 ? (K + 127) / 128 : K / 32;
-}
-template <int WT>
-__device__ __forceinline__ Mat w13_mat(const uint8_t* slot, int H, int Ie) {
-  const size_t t13 = (size_t)(2 * Ie / 16) * ksteps<WT>(H), t2 = (size_t)(H / 16) * ksteps<WT>(Ie);
-  Mat m;
-  m.codes = make_rsrc(slot, t13 * 1024);
-  m.scales = make_rsrc(WT == W_MXFP4 ? slot + (t13 + t2) * 1024 : slot, WT == W_MXFP4 ? t13 * 64 : 0);
-  m.nK = ksteps<WT>(H);
-  m.K = H;
-  return m;
-}
-template <int WT>
-__device__ __forceinline__ Mat w2_mat(const uint8_t* slot, int H, int Ie) {
-  const size_t t13 = (size_t)(2 * Ie / 16) * ksteps<WT>(H), t2 = (size_t)(H / 16) * ksteps<WT>(Ie);
-  Mat m;
-  m.codes = make_rsrc(slot + t13 * 1024, t2 * 1024);
-  m.scales = make_rsrc(WT == W_MXFP4 ? slot + (t13 + t2) * 1024 + t13 * 64 : slot, WT == W_MXFP4 ? t2 * 64 : 0);
-  m.nK = ksteps<WT>(Ie);
-  m.K = Ie;
-  return m;
 }
 
 // Block shape (both phases): 4 waves.  Each wave owns R row tiles of 16 rows;

@@ -18,6 +18,10 @@ hipError_t launch_combine(const float* rows, const float* w, const int32_t* inv,
 // Grouped FFN phases.  wtype: 0 f32, 1 bf16, 2 mxfp4.
 hipError_t launch_ffn_gate_up(int wtype, const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_down(int wtype, const FfnArgs& a, hipStream_t st);
+// Prefill-sized batches (LDS-staged token tiles); same arguments and results.
+bool prefill_supported(int wtype, int H, int I, int I_shared);
+hipError_t launch_prefill_gate_up(int wtype, const FfnArgs& a, hipStream_t st);
+hipError_t launch_prefill_down(int wtype, const FfnArgs& a, hipStream_t st);
 // Workspace bytes (the SwiGLU intermediate for T*k routed + T shared rows).
 size_t ffn_workspace_bytes(int wtype, int T, int k, int I, int I_shared);
 

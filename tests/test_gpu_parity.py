@@ -119,6 +119,11 @@ SMALL = [
     (synth.MXFP4, 40, 160, 96, 8, 3, True),     # 4-tile down blocks over 10 row tiles: ragged last block
     (synth.BF16, 20, 160, 96, 8, 3, True),
     (synth.F32, 9, 64, 32, 5, 2, True),
+    # prefill-sized batches (>= 32 pairs per expert): LDS-staged kernels, token passes of 128
+    (synth.BF16, 512, 256, 256, 8, 2, False),
+    (synth.BF16, 300, 384, 128, 4, 2, True),
+    (synth.MXFP4, 600, 512, 256, 16, 4, True),
+    (synth.MXFP4, 257, 256, 384, 8, 1, False),
 ]
 
 
