@@ -74,6 +74,15 @@ __device__ __forceinline__ const uint8_t* uniform(const uint8_t* p) {
   return (const uint8_t*)(((uint64_t)hi << 32) | lo);
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every global load still in flight, which would drain a software
+// prefetch pipeline at each barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

@@ -143,7 +143,7 @@ __device__ __forceinline__ void load_chunk(Chunk<WT, NT, R, U>& c, const Mat& w,
       const int du = CLAMP ? min(s + u, s1 - 1) - s : u;
       c.qa[u][t] = bld16(w.codes, lane * 16, (tile_step + du) * 1024);
       if constexpr (WT == W_MXFP4)
-        c.qs[u][t] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(w.scales, lane, (tile_step + du) * 64, 0);
+        c.qs[u][t] = load_scale_word(w.scales, lane, (tile_step + du) * 64);
       else
         c.qs[u][t] = 0u;
     }
@@ -174,6 +174,7 @@ template <int WT, int NT, int R, int U>
 __device__ __forceinline__ void compute_chunk(const Chunk<WT, NT, R, U>& c, int s, int s1, int ntl,
                                               f32x4 (&acc)[R][NT]) {
   constexpr int NA = Chunk<WT, NT, R, U>::NA;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (s + u < s1) {
@@ -183,7 +184,7 @@ __device__ __forceinline__ void compute_chunk(const Chunk<WT, NT, R, U>& c, int 
         if constexpr (WT == W_BF16) {
           A[0] = as_bf16x8(c.qa[u][t]);
         } else {
-          const float sc = e8m0_to_f32(c.qs[u][t]);
+          const float sc = scale_of_word(c.qs[u][t], lane);
 #pragma unroll
           for (int m = 0; m < 4; ++m) A[m] = fp4x8_to_bf16x8(c.qa[u][t][m], sc);
         }

@@ -92,6 +92,17 @@ __device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int voff, int s
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// Block scale of this lane's MXFP4 fragment.  A tile's 64 scale bytes are read
+// as 16 words, each lane loading the word that holds its byte; the byte is only
+// picked out where the scale is used, so the wait for the load stays there too
+// (a byte load is widened right after it is issued, which forces an early wait).
+__device__ __forceinline__ uint32_t load_scale_word(__amdgpu_buffer_rsrc_t r, int lane, int soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, lane & ~3, soff, 0);
+}
+__device__ __forceinline__ float scale_of_word(uint32_t word, int lane) {
+  return e8m0_to_f32((word >> (8 * (lane & 3))) & 0xffu);
+}
+
 // Column steps of a K-wide matrix and byte offsets inside an expert slot.
 template <int WT>
 __device__ __forceinline__ int ksteps(int K) {
