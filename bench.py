@@ -2,18 +2,28 @@
 """MoE-layer throughput on one MI355X, with the roofline of the dominant kernel
 and the CPU oracle timed beside it.
 
-Default workload: the bf16 decode layer (hidden 2048, 256 routed experts plus one
-always-on shared expert, top-8, expert intermediate 512) at 16 tokens per layer,
-stacked as 16 layers with distinct weights (16 replicas of the 257 experts, 26 GB)
-so that the 256 MB Infinity Cache cannot serve re-used weights.  A step is one
-pass of the whole path (top-k, permutation, grouped FFN gate_up + down, combine)
-through the 16 layers; every layer has its own seeded logits and activations,
-all resident in HBM before the timed region.  All experts are resident (fixed
-identity slot table, no cache misses), as the workload specifies.
+Default workload (--workload decode_bf16): the bf16 decode layer (hidden 2048,
+256 routed experts plus one always-on shared expert, top-8, expert intermediate
+512) at 16 tokens per layer, stacked as 16 layers with distinct weights (16
+replicas of the 257 experts, 26 GB) so that the 256 MB Infinity Cache cannot
+serve re-used weights.  A step is one pass of the whole path (top-k,
+permutation, grouped FFN gate_up + down, combine) through the 16 layers; every
+layer has its own seeded logits and activations, all resident in HBM before the
+timed region.  All experts are resident (fixed identity slot table).
 
-Prints one JSON line.
+Other workloads, each printing one JSON line of the same form:
+  decode_mxfp4       43 stacked MXFP4 layers (hidden 4096, 256 experts, top-6,
+                     intermediate 2048), all 11,008 experts resident, Zipf(1.1)
+                     popularity + N(0,1) logits, batches 64, 1 and 8.
+  prefill_mxfp4      4096-token layers of that shape; each layer's weights come
+                     from pinned host memory into one of two HBM banks while the
+                     previous layer computes (43 layers).
+  cached_trace_bf16  1000 single-token steps through 48 bf16 layers with a cold
+                     global-LRU slot cache holding 37% of the experts.
+  hostbw             pinned host -> HBM copy bandwidth at the fill sizes.
 """
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -25,23 +35,36 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE-layer tokens/s at 1 MI355X; % HBM BW (decode), % MFMA peak (prefill)"
 COUNTERS = os.path.join(ROOT, "profiles", "gate_up_mfma_bf16_decode_T16_counters.txt")
-FFN_SOURCES = [os.path.join(ROOT, "routed_expert_ffn_layer_amd", "csrc", f) for f in ("ffn.hip", "common.hpp")]
+FFN_SOURCES = [os.path.join(ROOT, "routed_expert_ffn_layer_amd", "csrc", f)
+               for f in ("ffn.hip", "ffn_common.hpp", "common.hpp")]
+WORKLOADS = ("decode_bf16", "decode_mxfp4", "prefill_mxfp4", "cached_trace_bf16", "hostbw")
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--tokens", type=int, default=16, help="tokens per layer (decode batch)")
-    ap.add_argument("--layers", type=int, default=16, help="stacked layers with distinct weights")
-    ap.add_argument("--extra-batches", default="1,4", help="other decode batches to report (not timed as value)")
+    ap.add_argument("--workload", choices=WORKLOADS, default="decode_bf16")
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default depends on the workload)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default depends on the workload)")
+    ap.add_argument("--tokens", type=int, default=None, help="tokens per layer of the headline batch")
+    ap.add_argument("--layers", type=int, default=None, help="stacked layers")
+    ap.add_argument("--extra-batches", default=None, help="other decode batches to report")
+    ap.add_argument("--host-layers", type=int, default=None,
+                    help="distinct layers kept in pinned host memory (layer l reads host layer l mod this)")
+    ap.add_argument("--distinct-experts", type=int, default=512,
+                    help="decode_mxfp4: distinct generated experts copied into the 11,008 slots")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def ffn_source_hash():
@@ -76,26 +99,67 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
 
 
-def gate_up_bytes(n_experts_active, has_shared, T, k, H, I):
-    """Algorithmic HBM bytes of one gate_up launch: each active expert's W13 once
-    (2*I*H bf16), the T token rows of x, the SwiGLU intermediate written."""
+def out_line(value, unit, steps, warmup, ms_per_step, dtype, data, config, roofline, cpu, **extra):
+    d = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
+         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+         "dtype": dtype, "data": data, "config": config, "roofline": roofline}
+    d.update(extra)
+    d["cpu_baseline"] = cpu
+    return d
+
+
+def time_back_to_back(fn, n_calls, passes):
+    """Average duration of fn(i) for i < n_calls, launched back to back on the
+    current stream; one event pair around each whole pass."""
+    import torch
+    for i in range(n_calls):
+        fn(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(passes):
+        for i in range(n_calls):
+            fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (passes * n_calls)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work.
+
+def w13_bytes(wdt, H, I):
+    """Bytes of the gate/up half of an expert slot (codes and, for MXFP4, scales)."""
+    import synth
+    o = synth.slot_offsets(wdt, H, I)
+    if wdt == synth.MXFP4:
+        return (o["w2"] - o["w13"]) + (o["s2"] - o["s13"])
+    return o["w2"] - o["w13"]
+
+
+def gate_up_bytes(wdt, n_experts_active, has_shared, T, k, H, I):
+    """Algorithmic HBM bytes of one gate_up launch: each active expert's W13 once,
+    the T token rows of x, the SwiGLU intermediate written (bf16)."""
     experts = n_experts_active + (1 if has_shared else 0)
     rows = T * k + (T if has_shared else 0)
-    return experts * 2 * I * H * 2 + T * H * 2 + rows * I * 2
+    return experts * w13_bytes(wdt, H, I) + T * H * 2 + rows * I * 2
 
 
-def layer_bytes(n_experts_active, has_shared, T, k, H, I):
+def layer_bytes(wdt, n_experts_active, has_shared, T, k, E, H, I):
     """Algorithmic HBM bytes of the whole layer: every active expert's weights once,
     logits, x, the intermediate (write + read), expert output rows (write + read),
     gate weights and the bf16 layer output."""
+    import synth
     experts = n_experts_active + (1 if has_shared else 0)
     rows = T * k + (T if has_shared else 0)
-    w = experts * 3 * I * H * 2
-    act = T * 256 * 4 + T * H * 2 + 2 * rows * I * 2 + 2 * rows * H * 4 + T * H * 2
+    w = experts * synth.expert_bytes(wdt, H, I)
+    act = T * E * 4 + T * H * 2 + 2 * rows * I * 2 + 2 * rows * H * 4 + T * k * 4 + T * H * 2
     return w + act
 
 
-def run_decode(args, T, n_layers, steps, warmup, time_kernel=True):
+# ---------------------------------------------------------------------------
+# decode_bf16 (the headline workload).
+
+def run_decode_bf16(T, n_layers, steps, warmup, time_kernel=True):
     import torch
     import synth
     from routed_expert_ffn_layer_amd import layer as L
@@ -112,6 +176,11 @@ def run_decode(args, T, n_layers, steps, warmup, time_kernel=True):
                            .view(np.int16)).to(dev) for l in range(n_layers)]
     slots = L.identity_slots(E, dev)
 
+    def gate_up(l):
+        b = bufs[l]
+        moe.moe_grouped_ffn_gate_up(b.wdt, pools[l][:E], stride, slots, pools[l][E], I, xs[l], b.offsets,
+                                    b.sorted_rows, T, k, E, H, I, b.out_rows, b.shared_out, b.workspace)
+
     def step():
         for l in range(n_layers):
             b = bufs[l]
@@ -120,11 +189,6 @@ def run_decode(args, T, n_layers, steps, warmup, time_kernel=True):
             moe.moe_grouped_ffn_down(b.wdt, pools[l][:E], stride, slots, pools[l][E], I, xs[l], b.offsets,
                                      b.sorted_rows, T, k, E, H, I, b.out_rows, b.shared_out, b.workspace)
             L.combine(b, True)
-
-    def gate_up(l):
-        b = bufs[l]
-        moe.moe_grouped_ffn_gate_up(b.wdt, pools[l][:E], stride, slots, pools[l][E], I, xs[l], b.offsets,
-                                    b.sorted_rows, T, k, E, H, I, b.out_rows, b.shared_out, b.workspace)
 
     for _ in range(warmup):
         step()
@@ -137,7 +201,7 @@ def run_decode(args, T, n_layers, steps, warmup, time_kernel=True):
     active = [int((b.counts > 0).sum().item()) for b in bufs]
     res = dict(T=T, layers=n_layers, steps=steps, seconds=elapsed, ms_per_step=1e3 * elapsed / steps,
                layer_tokens_per_s=T * n_layers * steps / elapsed, active_experts_mean=float(np.mean(active)))
-    step_bytes = sum(layer_bytes(a, True, T, k, H, I) for a in active)
+    step_bytes = sum(layer_bytes(synth.BF16, a, True, T, k, E, H, I) for a in active)
     res["layer_hbm_gbs"] = step_bytes * steps / elapsed / 1e9
     if time_kernel:
         # The dominant kernel, timed live on its launch stream: the same layers'
@@ -145,17 +209,8 @@ def run_decode(args, T, n_layers, steps, warmup, time_kernel=True):
         # steps), one event pair around each pass of n_layers launches, so the
         # events add no gap between launches and their own cost spreads over the pass.
         passes = max(4, steps // 4)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for l in range(n_layers):
-            gate_up(l)
-        e0.record()
-        for _ in range(passes):
-            for l in range(n_layers):
-                gate_up(l)
-        e1.record()
-        torch.cuda.synchronize()
-        per_launch = e0.elapsed_time(e1) * 1e-3 / (passes * n_layers)
-        gb = float(np.mean([gate_up_bytes(a, True, T, k, H, I) for a in active]))
+        per_launch = time_back_to_back(gate_up, n_layers, passes)
+        gb = float(np.mean([gate_up_bytes(synth.BF16, a, True, T, k, H, I) for a in active]))
         res["gate_up_avg_us"] = per_launch * 1e6
         res["gate_up_bytes_avg"] = gb
         res["gate_up_gbs"] = gb / per_launch / 1e9
@@ -165,7 +220,7 @@ def run_decode(args, T, n_layers, steps, warmup, time_kernel=True):
     return res
 
 
-def cpu_baseline(seconds):
+def cpu_decode_bf16(seconds):
     """The oracle (plain fp64 C, one thread) on a bounded sample of the same
     workload: decode layers of 16 tokens with the same shapes, until the budget
     is spent."""
@@ -198,6 +253,487 @@ def cpu_baseline(seconds):
                        f"fp64 C oracle, single thread, {el:.1f} s")
 
 
+def workload_decode_bf16(args):
+    T = args.tokens or 16
+    n_layers = args.layers or 16
+    steps, warmup = args.steps or 50, 5 if args.warmup is None else args.warmup
+    extra = [int(v) for v in (args.extra_batches or "1,4").split(",") if v.strip()]
+    main_res = run_decode_bf16(T, n_layers, steps, warmup)
+    keys = ("layer_tokens_per_s", "ms_per_step", "layer_hbm_gbs", "gate_up_gbs", "gate_up_avg_us",
+            "active_experts_mean")
+    by_batch = {str(T): {k: main_res[k] for k in keys}}
+    for tb in extra:
+        if tb == T:
+            continue
+        r = run_decode_bf16(tb, n_layers, max(10, steps // 2), 2)
+        by_batch[str(tb)] = {k: r[k] for k in keys}
+    cpu = None if args.no_cpu_baseline else cpu_decode_bf16(args.cpu_seconds)
+    achieved = main_res["gate_up_gbs"]
+    return out_line(
+        main_res["layer_tokens_per_s"], "layer-tokens/s", steps, warmup, main_res["ms_per_step"], "bf16",
+        "synthetic (seeded N(0,0.02) weights, N(0,1) logits and activations)",
+        {"workload": "decode layer bf16: hidden 2048, 256 routed experts + 1 shared, top-8, intermediate 512",
+         "tokens_per_layer": T, "stacked_layers": n_layers,
+         "weights_in_hbm_gb": round(n_layers * 257 * 6291456 / 1e9, 2), "slots": "all resident"},
+        {"kernel": "gate_up_mfma<bf16> (moe_grouped_ffn_gate_up)", "bound": "hbm", "achieved": achieved,
+         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+         "avg_launch_us": main_res["gate_up_avg_us"], "algorithmic_bytes_per_launch": main_res["gate_up_bytes_avg"],
+         "launches_timed": main_res["gate_up_launches_timed"],
+         "timing": "events around back-to-back passes of the timed layers' gate_up launches"},
+        cpu, layer_hbm_frac=main_res["layer_hbm_gbs"] / HBM_PEAK_GBS, by_batch=by_batch)
+
+
+# ---------------------------------------------------------------------------
+# decode_mxfp4: 43 stacked layers, every expert resident.
+
+def mxfp4_resident_stack(c, n_layers, n_distinct, dev):
+    """[n_layers * E][expert_bytes] uint8 in HBM.  n_distinct experts are generated
+    (N(0, 0.02) -> MXFP4) and copied into the slots, slot s of layer l taking
+    distinct expert (7 s + 131 l) mod n_distinct: every slot is its own address,
+    so the bytes a layer streams are its own."""
+    import torch
+    import synth
+    H, I, E = c["H"], c["I"], c["E"]
+    eb = synth.expert_bytes(synth.MXFP4, H, I)
+    distinct = torch.empty((n_distinct, eb), dtype=torch.uint8, device=dev)
+    for j in range(0, n_distinct, 256):
+        n = min(256, n_distinct - j)
+        distinct[j:j + n].copy_(synth.torch_mxfp4_expert_pool(n, H, I, seed=c["seed"] * 100 + j // 256, device=dev))
+        progress(f"generated {j + n}/{n_distinct} distinct MXFP4 experts")
+    stack = torch.empty((n_layers * E, eb), dtype=torch.uint8, device=dev)
+    for l in range(n_layers):
+        idx = (torch.arange(E, device=dev) * 7 + 131 * l) % n_distinct
+        torch.index_select(distinct, 0, idx, out=stack[l * E:(l + 1) * E])
+        if l % 8 == 7 or l == n_layers - 1:
+            torch.cuda.synchronize()
+            progress(f"filled {l + 1}/{n_layers} resident layers")
+    return stack, distinct
+
+
+def run_decode_mxfp4(stack, c, T, n_layers, steps, warmup, n_batches=4):
+    import torch
+    import synth
+    from routed_expert_ffn_layer_amd import layer as L
+    from routed_expert_ffn_layer_amd import moe
+    H, I, E, k = c["H"], c["I"], c["E"], c["k"]
+    dev = stack.device
+    eb = synth.expert_bytes(synth.MXFP4, H, I)
+    bufs = [L.LayerBuffers(T, E, k, H, I, moe.MOE_MXFP4) for _ in range(n_layers)]
+    logits = [[torch.from_numpy(synth.zipf_noise_logits(c["seed"], T, E, l, c["zipf_s"], batch=bi)).to(dev)
+               for bi in range(n_batches)] for l in range(n_layers)]
+    xs = [torch.from_numpy(synth.encode_activations(synth.BF16, synth.normal_x(c["seed"], T, H, 7, bi))
+                           .view(np.int16)).to(dev) for bi in range(n_batches)]
+    slots = L.identity_slots(E, dev)
+    pools = [stack[l * E:(l + 1) * E] for l in range(n_layers)]
+
+    def step(j):
+        bi = j % n_batches
+        for l in range(n_layers):
+            L.forward(bufs[l], logits[l][bi], xs[bi], pools[l], eb, slots)
+
+    for j in range(warmup):
+        step(j)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(steps):
+        step(j)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # routing of every (layer, batch), for the algorithmic bytes of the timed steps
+    active = np.zeros((n_layers, n_batches))
+    for bi in range(n_batches):
+        for l in range(n_layers):
+            L.route(bufs[l], logits[l][bi])
+            active[l, bi] = int((bufs[l].counts > 0).sum().item())
+    step_bytes = [sum(layer_bytes(synth.MXFP4, active[l, bi], False, T, k, E, H, I) for l in range(n_layers))
+                  for bi in range(n_batches)]
+    total_bytes = sum(step_bytes[j % n_batches] for j in range(steps))
+
+    # the FFN kernels of every layer on batch 0's routing, back to back
+    for l in range(n_layers):
+        L.route(bufs[l], logits[l][0])
+
+    def gate_up(l):
+        b = bufs[l]
+        moe.moe_grouped_ffn_gate_up(b.wdt, pools[l], eb, slots, None, 0, xs[0], b.offsets, b.sorted_rows,
+                                    T, k, E, H, I, b.out_rows, None, b.workspace)
+
+    def down(l):
+        b = bufs[l]
+        moe.moe_grouped_ffn_down(b.wdt, pools[l], eb, slots, None, 0, xs[0], b.offsets, b.sorted_rows,
+                                 T, k, E, H, I, b.out_rows, None, b.workspace)
+
+    passes = 4
+    gu = time_back_to_back(gate_up, n_layers, passes)
+    dn = time_back_to_back(down, n_layers, passes)
+    gub = float(np.mean([gate_up_bytes(synth.MXFP4, active[l, 0], False, T, k, H, I) for l in range(n_layers)]))
+    w2b = eb - w13_bytes(synth.MXFP4, H, I)
+    dnb = float(np.mean([active[l, 0] * w2b + T * k * I * 2 + T * k * H * 4 for l in range(n_layers)]))
+    return dict(T=T, layers=n_layers, steps=steps, seconds=elapsed, ms_per_step=1e3 * elapsed / steps,
+                layer_tokens_per_s=T * n_layers * steps / elapsed, stack_tokens_per_s=T * steps / elapsed,
+                layer_hbm_gbs=total_bytes / elapsed / 1e9, active_experts_mean=float(active.mean()),
+                gate_up_avg_us=gu * 1e6, gate_up_bytes_avg=gub, gate_up_gbs=gub / gu / 1e9,
+                down_avg_us=dn * 1e6, down_gbs=dnb / dn / 1e9, gate_up_launches_timed=passes * n_layers)
+
+
+def cpu_decode_mxfp4(stack, c, T, seconds):
+    """The oracle on a bounded sample: MXFP4 decode layers of T tokens (layer 0's
+    experts, copied from HBM), until the budget is spent."""
+    import synth
+    import oracle
+    H, I, E, k = c["H"], c["I"], c["E"], c["k"]
+    logits = synth.zipf_noise_logits(c["seed"], T, E, 0, c["zipf_s"], batch=0)
+    ids, _, _ = oracle.route_topk(logits, k)
+    used = sorted(set(ids.ravel().tolist()))
+    eb = synth.expert_bytes(synth.MXFP4, H, I)
+    blank = np.zeros(eb, np.uint8)
+    experts = [blank] * E
+    for e in used:
+        experts[e] = stack[e].cpu().numpy()
+    x = synth.encode_activations(synth.BF16, synth.normal_x(c["seed"], T, H, 7, 0))
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.layer(synth.MXFP4, experts, x, logits, k, H, I)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 20:
+            break
+    return dict(value=T * n / el, unit="layer-tokens/s", cores=1, kind="oracle",
+                sample=f"{n} MXFP4 decode layers of {T} tokens ({len(used)} active experts of {E}, H={H}, I={I}, "
+                       f"top-{k}), fp64 C oracle, single thread, {el:.1f} s")
+
+
+def workload_decode_mxfp4(args):
+    import torch
+    import synth
+    c = synth.CONFIGS["decode_mxfp4"]
+    n_layers = args.layers or c["layers"]
+    steps, warmup = args.steps or 10, 2 if args.warmup is None else args.warmup
+    T = args.tokens or 64
+    batches = [T] + [int(v) for v in (args.extra_batches or "1,8").split(",") if v.strip() and int(v) != T]
+    dev = torch.device("cuda:0")
+    stack, distinct = mxfp4_resident_stack(c, n_layers, args.distinct_experts, dev)
+    del distinct
+    torch.cuda.empty_cache()
+    res = {}
+    for tb in batches:
+        progress(f"decode_mxfp4: T={tb}")
+        res[tb] = run_decode_mxfp4(stack, c, tb, n_layers, steps if tb == T else max(4, steps // 2), warmup)
+    cpu = None if args.no_cpu_baseline else cpu_decode_mxfp4(stack, c, 8, args.cpu_seconds)
+    m = res[T]
+    keys = ("layer_tokens_per_s", "stack_tokens_per_s", "ms_per_step", "layer_hbm_gbs", "gate_up_gbs",
+            "gate_up_avg_us", "down_gbs", "down_avg_us", "active_experts_mean")
+    return out_line(
+        m["layer_tokens_per_s"], "layer-tokens/s", steps, warmup, m["ms_per_step"], "bf16 (MXFP4 weights)",
+        f"synthetic (seeded N(0,0.02) weights quantized to MXFP4, {args.distinct_experts} distinct experts copied "
+        "into every slot; Zipf(1.1) popularity + N(0,1) logits, 4 batches per layer cycled; N(0,1) activations)",
+        {"workload": "decode layer MXFP4: hidden 4096, 256 routed experts, top-6, intermediate 2048",
+         "tokens_per_layer": T, "stacked_layers": n_layers,
+         "weights_in_hbm_gb": round(stack.numel() / 1e9, 2), "slots": "all resident"},
+        {"kernel": "gate_up_mfma<mxfp4> (moe_grouped_ffn_gate_up)", "bound": "hbm", "achieved": m["gate_up_gbs"],
+         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": m["gate_up_gbs"] / HBM_PEAK_GBS, "traffic": None,
+         "avg_launch_us": m["gate_up_avg_us"], "algorithmic_bytes_per_launch": m["gate_up_bytes_avg"],
+         "launches_timed": m["gate_up_launches_timed"],
+         "timing": "events around back-to-back passes of the stack's gate_up launches"},
+        cpu, layer_hbm_frac=m["layer_hbm_gbs"] / HBM_PEAK_GBS,
+        by_batch={str(tb): {k: r[k] for k in keys} for tb, r in res.items()})
+
+
+# ---------------------------------------------------------------------------
+# hostbw: pinned host -> HBM copies.
+
+def host_to_device_gbs(nbytes, reps=None):
+    """GB/s of hipMemcpyAsync from pinned host memory into HBM (torch copy_ with
+    non_blocking on a side stream), reps copies back to back."""
+    import torch
+    reps = reps or max(3, min(50, int(2e9 // nbytes)))
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    src.fill_(3)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dst.copy_(src, non_blocking=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src, non_blocking=True)
+        e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3
+    del src, dst
+    return nbytes * reps / sec / 1e9
+
+
+def workload_hostbw(args):
+    import synth
+    sizes = {"bf16_expert": synth.expert_bytes(synth.BF16, 2048, 512),
+             "mxfp4_expert": synth.expert_bytes(synth.MXFP4, 4096, 2048),
+             "mxfp4_layer": 256 * synth.expert_bytes(synth.MXFP4, 4096, 2048)}
+    res = {}
+    for name, n in sizes.items():
+        res[name] = {"bytes": n, "gbs": host_to_device_gbs(n)}
+        progress(f"hostbw {name}: {res[name]['gbs']:.1f} GB/s")
+    big = res["mxfp4_layer"]["gbs"]
+    return out_line(big, "GB/s", 1, 1, None, "u8", "synthetic (constant bytes)",
+                    {"workload": "pinned host -> HBM hipMemcpyAsync at the fill sizes"},
+                    None, None, by_size=res)
+
+
+# ---------------------------------------------------------------------------
+# prefill_mxfp4: double-buffered layer streaming around 4096-token layers.
+
+def workload_prefill_mxfp4(args):
+    import torch
+    import synth
+    from routed_expert_ffn_layer_amd import layer as L
+    from routed_expert_ffn_layer_amd import moe
+    c = synth.CONFIGS["prefill_mxfp4"]
+    H, I, E, k, T = c["H"], c["I"], c["E"], c["k"], args.tokens or c["T"]
+    n_layers = args.layers or c["layers"]
+    n_host = args.host_layers or 2
+    steps, warmup = args.steps or 2, 1 if args.warmup is None else args.warmup
+    dev = torch.device("cuda:0")
+    eb = synth.expert_bytes(synth.MXFP4, H, I)
+    lb = E * eb
+    # pinned host layers (layer l streams host layer l mod n_host)
+    host = []
+    for j in range(n_host):
+        h = torch.empty((E, eb), dtype=torch.uint8, pin_memory=True)
+        h.copy_(synth.torch_mxfp4_expert_pool(E, H, I, seed=c["seed"] * 100 + j, device=dev).cpu())
+        host.append(h)
+        progress(f"host layer {j + 1}/{n_host} ready ({lb / 1e9:.2f} GB pinned)")
+    banks = [torch.empty((E, eb), dtype=torch.uint8, device=dev) for _ in range(2)]
+    ptrs = (ctypes.c_void_p * n_layers)(*[host[l % n_host].data_ptr() for l in range(n_layers)])
+    fill_stream = torch.cuda.Stream()
+    ls = moe.LayerStream(n_layers, lb, banks[0], banks[1], fill_stream, host_layer_ptrs=ptrs)
+    b = L.LayerBuffers(T, E, k, H, I, moe.MOE_MXFP4)
+    n_x = 4
+    logits = [torch.from_numpy(synth.normal_logits(c["seed"], T, E, 7, l)).to(dev) for l in range(n_layers)]
+    xs = [torch.from_numpy(synth.encode_activations(synth.BF16, synth.normal_x(c["seed"], T, H, 7, j))
+                           .view(np.int16)).to(dev) for j in range(n_x)]
+    slots = L.identity_slots(E, dev)
+    comp = torch.cuda.current_stream()
+
+    def compute(l, bank):
+        L.forward(b, logits[l], xs[l % n_x], banks[bank], eb, slots)
+
+    def pipelined():
+        ls.fill(0, 0)
+        for l in range(n_layers):
+            if l + 1 < n_layers:
+                ls.fill(l + 1, (l + 1) % 2)
+            ls.acquire(l % 2, comp)
+            compute(l, l % 2)
+            ls.release(l % 2, comp)
+        torch.cuda.synchronize()
+
+    for _ in range(warmup):
+        pipelined()
+    progress("prefill: pipelined warm")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        pipelined()
+    t_pipe = (time.perf_counter() - t0) / steps
+    progress(f"prefill: pipelined {t_pipe * 1e3:.1f} ms per {n_layers} layers")
+    # fills alone
+    t0 = time.perf_counter()
+    for l in range(n_layers):
+        ls.fill(l, l % 2)
+    torch.cuda.synchronize()
+    t_fill = time.perf_counter() - t0
+    # compute alone (weights already in bank 0)
+    ls.fill(0, 0)
+    ls.acquire(0, comp)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for l in range(n_layers):
+        compute(l, 0)
+    torch.cuda.synchronize()
+    t_gemm = time.perf_counter() - t0
+    ls.release(0, comp)
+    progress(f"prefill: fills alone {t_fill * 1e3:.1f} ms, compute alone {t_gemm * 1e3:.1f} ms")
+    # the grouped GEMM kernels alone, back to back on layer 0's routing
+    L.route(b, logits[0])
+
+    def gate_up(_):
+        moe.moe_grouped_ffn_gate_up(b.wdt, banks[0], eb, slots, None, 0, xs[0], b.offsets, b.sorted_rows,
+                                    T, k, E, H, I, b.out_rows, None, b.workspace)
+
+    def down(_):
+        moe.moe_grouped_ffn_down(b.wdt, banks[0], eb, slots, None, 0, xs[0], b.offsets, b.sorted_rows,
+                                 T, k, E, H, I, b.out_rows, None, b.workspace)
+
+    gu = time_back_to_back(gate_up, 1, 10)
+    dn = time_back_to_back(down, 1, 10)
+    gu_flop = 2.0 * T * k * 2 * I * H
+    dn_flop = 2.0 * T * k * I * H
+    layer_flop = gu_flop + dn_flop
+    bp = host_to_device_gbs(lb, reps=3)
+    ls.close()
+    cpu = None if args.no_cpu_baseline else cpu_prefill_mxfp4(banks[0], logits[0], xs[0], c, T, args.cpu_seconds)
+    gu_tf = gu_flop / gu / 1e12
+    return out_line(
+        T * n_layers / t_pipe, "layer-tokens/s", steps, warmup, t_pipe * 1e3, "bf16 (MXFP4 weights)",
+        f"synthetic (seeded N(0,0.02) weights quantized to MXFP4, {n_host} distinct pinned host layers streamed "
+        "as layer l mod that; N(0,1) logits and activations)",
+        {"workload": "prefill layer MXFP4: hidden 4096, 256 routed experts, top-6, intermediate 2048",
+         "tokens_per_layer": T, "stacked_layers": n_layers, "host_layers_distinct": n_host,
+         "layer_bytes": lb, "slots": "two HBM banks, one layer each"},
+        {"kernel": "prefill_gate_up<mxfp4> (moe_grouped_ffn_gate_up)", "bound": "mfma", "achieved": gu_tf,
+         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": gu_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+         "avg_launch_us": gu * 1e6, "algorithmic_flop_per_launch": gu_flop, "launches_timed": 10,
+         "timing": "events around back-to-back gate_up launches on one layer's routing"},
+        cpu,
+        stack_tokens_per_s=T / t_pipe,
+        pipeline={"t_overlapped_ms": t_pipe * 1e3, "t_fill_alone_ms": t_fill * 1e3, "t_gemm_alone_ms": t_gemm * 1e3,
+                  "overlap_penalty": t_pipe / max(t_fill, t_gemm) - 1.0,
+                  "fill_gbs": lb * n_layers / t_fill / 1e9, "host_to_device_gbs": bp},
+        grouped_gemm={"gate_up_us": gu * 1e6, "down_us": dn * 1e6,
+                      "tflops": layer_flop / (gu + dn) / 1e12,
+                      "mfma_frac": layer_flop / (gu + dn) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                      "layer_tflops": layer_flop / (t_gemm / n_layers) / 1e12})
+
+
+def cpu_prefill_mxfp4(bank, logits_d, x_d, c, T, seconds):
+    """The oracle on a bounded sample of one prefill layer: routing of all T
+    tokens, then whole experts (each with all of its tokens) until the budget is
+    spent; the layer time is extrapolated from the measured seconds per routed
+    (token, expert) pair."""
+    import synth
+    import oracle
+    H, I, E, k = c["H"], c["I"], c["E"], c["k"]
+    logits = logits_d.cpu().numpy()
+    x = x_d.cpu().numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    ids, _, _ = oracle.route_topk(logits, k)
+    t_route = time.perf_counter() - t0
+    pairs, t_ffn, n_exp = 0, 0.0, 0
+    for e in range(E):
+        tok = np.nonzero((ids == e).any(axis=1))[0].astype(np.int32)
+        if tok.size == 0:
+            continue
+        w = bank[e].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.expert_rows(synth.MXFP4, w, H, I, x, tok)
+        t_ffn += time.perf_counter() - t0
+        pairs += tok.size
+        n_exp += 1
+        if t_ffn >= seconds:
+            break
+    layer_s = t_route + t_ffn / pairs * T * k
+    return dict(value=T / layer_s, unit="layer-tokens/s", cores=1, kind="oracle",
+                sample=f"routing of {T} tokens + {n_exp} experts with {pairs} routed tokens of one MXFP4 prefill "
+                       f"layer (H={H}, I={I}), fp64 C oracle, single thread, {t_route + t_ffn:.1f} s; layer time "
+                       f"extrapolated to {T * k} routed tokens")
+
+
+# ---------------------------------------------------------------------------
+# cached_trace_bf16: 1000 single-token steps through a cold global-LRU cache.
+
+def workload_cached_trace_bf16(args):
+    import torch
+    import synth
+    from routed_expert_ffn_layer_amd import layer as L
+    from routed_expert_ffn_layer_amd import moe
+    c = synth.CONFIGS["cached_trace_bf16"]
+    H, I, E, k = c["H"], c["I"], c["E"], c["k"]
+    n_layers = args.layers or c["layers"]
+    tokens = args.steps or c["tokens"]
+    warm_tokens = 20 if args.warmup is None else args.warmup
+    n_host = args.host_layers or 8
+    S = synth.cache_slots_for(c)
+    dev = torch.device("cuda:0")
+    eb = synth.expert_bytes(synth.BF16, H, I)
+    stride = ((eb + 255) // 256) * 256
+    host = []
+    for j in range(n_host):
+        h = torch.empty((E, eb), dtype=torch.uint8, pin_memory=True)
+        h.copy_(synth.torch_bf16_expert_pool(E, H, I, seed=c["seed"] * 100 + j, device=dev).cpu())
+        host.append(h)
+    progress(f"cached trace: {n_host} pinned host layers ready")
+    ptrs = (ctypes.c_void_p * (n_layers * E))(
+        *[host[l % n_host].data_ptr() + e * eb for l in range(n_layers) for e in range(E)])
+    slot_pool = torch.empty((S, stride), dtype=torch.uint8, device=dev)
+    trace = synth.trace_logits(c["seed"], tokens, n_layers, E, c["zipf_s"], c["reuse_p"])
+    trace_d = torch.from_numpy(trace).to(dev)
+    xs = [torch.from_numpy(synth.encode_activations(synth.BF16, synth.normal_x(c["seed"], 1, H, 7, l))
+                           .view(np.int16)).to(dev) for l in range(n_layers)]
+    b = L.LayerBuffers(1, E, k, H, I, moe.MOE_BF16)
+
+    def run(cache, n_tok):
+        tot = dict(accesses=0, hits=0, misses=0, fill_bytes=0, waves=0)
+        for t in range(n_tok):
+            for l in range(n_layers):
+                _, waves = L.forward_cached(b, cache, l, trace_d[t, l:l + 1], xs[l], slot_pool, stride)
+                for key in ("accesses", "hits", "misses"):  # per step, repeated by every wave's call
+                    tot[key] += waves[0][key]
+                tot["fill_bytes"] += sum(w["fill_bytes"] for w in waves)
+                tot["waves"] += len(waves)
+        torch.cuda.synchronize()
+        return tot
+
+    fill_stream = torch.cuda.Stream()
+    warm = moe.MoeCache(n_layers, E, S, expert_bytes=eb, slot_stride=stride, slot_pool=slot_pool,
+                        host_expert_ptrs=ptrs, fill_stream=fill_stream)
+    run(warm, warm_tokens)
+    warm.close()
+    progress("cached trace: warm-up done; timing the cold cache")
+    cache = moe.MoeCache(n_layers, E, S, expert_bytes=eb, slot_stride=stride, slot_pool=slot_pool,
+                         host_expert_ptrs=ptrs, fill_stream=fill_stream)
+    t0 = time.perf_counter()
+    tot = run(cache, tokens)
+    el = time.perf_counter() - t0
+    cache.close()
+    progress(f"cached trace: {tokens} tokens in {el:.1f} s, miss rate {tot['misses'] / max(tot['accesses'], 1):.3f}")
+    bp = host_to_device_gbs(eb)
+    fill_gbs = tot["fill_bytes"] / el / 1e9
+    cpu = None if args.no_cpu_baseline else cpu_cached_trace(trace, host, c, n_layers, n_host, S, args.cpu_seconds)
+    return out_line(
+        tokens / el, "tokens/s", tokens, warm_tokens, el * 1e3 / tokens, "bf16",
+        f"synthetic (seeded N(0,0.02) weights, {n_host} distinct pinned host layers serving layer l mod that; "
+        "temporally correlated Zipf(1.0) Gumbel-top-k routing trace, reuse p=0.7)",
+        {"workload": "cached decode trace bf16: 1000 tokens x 48 layers, hidden 2048, 256 experts, top-8, "
+                     "intermediate 512, global LRU over 37% of the experts", "tokens": tokens,
+         "stacked_layers": n_layers, "slots": S, "slot_pool_gb": round(S * stride / 1e9, 2),
+         "host_layers_distinct": n_host},
+        {"kernel": "expert fills (hipMemcpyAsync pinned host -> HBM slots)", "bound": "pcie",
+         "achieved": fill_gbs, "peak": bp, "unit": "GB/s", "frac": fill_gbs / bp, "traffic": None,
+         "timing": "wall clock of the whole trace; peak = measured pinned host -> HBM bandwidth at one expert"},
+        cpu, layer_tokens_per_s=tokens * n_layers / el,
+        cache={"accesses": tot["accesses"], "hits": tot["hits"], "misses": tot["misses"],
+               "miss_rate": tot["misses"] / max(tot["accesses"], 1), "fill_bytes": tot["fill_bytes"],
+               "fill_gbs": fill_gbs, "host_to_device_gbs_one_expert": bp, "waves": tot["waves"],
+               "expert_read_gbs": tot["accesses"] * eb / el / 1e9})
+
+
+def cpu_cached_trace(trace, host, c, n_layers, n_host, S, seconds):
+    """The oracle on the first tokens of the same trace: its global LRU plus the
+    layer for every (token, layer), until the budget is spent."""
+    import synth
+    import oracle
+    H, I, E, k = c["H"], c["I"], c["E"], c["k"]
+    layers_host = [h.numpy() for h in host]
+    xs = [synth.encode_activations(synth.BF16, synth.normal_x(c["seed"], 1, H, 7, l)) for l in range(n_layers)]
+    lru = oracle.LRU(S, n_layers, E)
+    n = 0
+    t0 = time.perf_counter()
+    while n < trace.shape[0]:
+        for l in range(n_layers):
+            lg = trace[n, l:l + 1]
+            ids, _, _ = oracle.route_topk(lg, k)
+            counts = np.bincount(ids.ravel(), minlength=E).astype(np.int32)
+            lru.step(l, counts)
+            oracle.layer(synth.BF16, layers_host[l % n_host], xs[l], lg, k, H, I)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return dict(value=n / el, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {n} tokens of the trace through {n_layers} layers (oracle LRU + layer), fp64 C "
+                       f"oracle, single thread, {el:.1f} s")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -211,45 +747,10 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
-    main_res = run_decode(args, args.tokens, args.layers, args.steps, args.warmup)
-    by_batch = {str(args.tokens): {k: main_res[k] for k in ("layer_tokens_per_s", "ms_per_step", "layer_hbm_gbs",
-                                                           "gate_up_gbs", "gate_up_avg_us", "active_experts_mean")}}
-    for tb in [int(v) for v in args.extra_batches.split(",") if v.strip()]:
-        if tb == args.tokens:
-            continue
-        r = run_decode(args, tb, args.layers, max(10, args.steps // 2), 2)
-        by_batch[str(tb)] = {k: r[k] for k in ("layer_tokens_per_s", "ms_per_step", "layer_hbm_gbs", "gate_up_gbs",
-                                               "gate_up_avg_us", "active_experts_mean")}
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
-    achieved = main_res["gate_up_gbs"]
-    out = {
-        "metric": "MoE-layer tokens/s at 1 MI355X; % HBM BW (decode), % MFMA peak (prefill)",
-        "value": main_res["layer_tokens_per_s"],
-        "unit": "layer-tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": main_res["ms_per_step"],
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) logits and activations)",
-        "config": {"workload": "decode layer bf16: hidden 2048, 256 routed experts + 1 shared, top-8, "
-                               "intermediate 512", "tokens_per_layer": args.tokens,
-                   "stacked_layers": args.layers, "weights_in_hbm_gb": round(
-                       args.layers * 257 * 6291456 / 1e9, 2), "slots": "all resident"},
-        "roofline": {"kernel": "gate_up_mfma<bf16> (moe_grouped_ffn_gate_up)", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(), "avg_launch_us": main_res["gate_up_avg_us"],
-                     "algorithmic_bytes_per_launch": main_res["gate_up_bytes_avg"],
-                     "launches_timed": main_res["gate_up_launches_timed"],
-                     "timing": "events around back-to-back passes of the timed layers' gate_up launches"},
-        "layer_hbm_frac": main_res["layer_hbm_gbs"] / HBM_PEAK_GBS,
-        "by_batch": by_batch,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(out), flush=True)
+    fn = {"decode_bf16": workload_decode_bf16, "decode_mxfp4": workload_decode_mxfp4,
+          "prefill_mxfp4": workload_prefill_mxfp4, "cached_trace_bf16": workload_cached_trace_bf16,
+          "hostbw": workload_hostbw}[args.workload]
+    print(json.dumps(fn(args)), flush=True)
 
 
 if __name__ == "__main__":
