@@ -37,9 +37,12 @@
  *  stored row-tile major then column step; each tile is 64 fragments of 16 bytes
  *  in the order f = 16*g + row%16 with g = (k % KS) / (KS/4): a bf16 fragment is 8
  *  consecutive k, an MXFP4 fragment one 32-element block (OCP MX v1.0 E2M1,
- *  element 2i in the low nibble of byte i) whose E8M0 scale is byte f of the
- *  tile's 64-byte scale block.  This is the operand order of the bf16 MFMA, so a
- *  wave reads 1 KB of contiguous memory per load.  For bf16 and MXFP4, stored W13
+ *  element 2i in the low nibble of byte i).  This is the operand order of the
+ *  bf16 MFMA, so a wave reads 1 KB of contiguous memory per load.  MXFP4 E8M0
+ *  scales: per row tile the column steps are grouped 16 at a time into 1 KB scale
+ *  blocks (the last one padded), row-tile major; in a block, fragment f owns bytes
+ *  16f .. 16f+15, byte i being its scale at step 16*block + i, so one 16-byte load
+ *  per lane brings its scales for 16 steps.  For bf16 and MXFP4, stored W13
  *  row 16t+q is gate row 8t+q for q < 8 and up row 8t+q-8 otherwise.  W2 is the
  *  down projection.
  */

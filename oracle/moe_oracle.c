@@ -53,8 +53,11 @@ double ora_e8m0_value(uint8_t code) {
  * bytes are ordered by f = 16*g + (row % 16), where g = (k % KS) / (KS / 4) is
  * the column group: a bf16 fragment is 8 consecutive k, an MXFP4 fragment is
  * one 32-element block (element 2i in the low nibble of byte i).  An MXFP4 matrix
- * also has one E8M0 byte per fragment, in the same order.  If K is not a
- * multiple of 128 the last MXFP4 step is padded with zero fragments. */
+ * also has one E8M0 byte per fragment, stored apart from the codes: per row tile
+ * the column steps are grouped 16 at a time into 1 KB scale blocks, in which
+ * fragment f owns bytes 16f .. 16f+15, byte i holding its scale at step
+ * 16*block + i (steps past the last one are padding).  If K is not a multiple of
+ * 128 the last MXFP4 step is padded with zero fragments. */
 static size_t ksteps(int dtype, int K) { return dtype == ORA_MXFP4 ? (size_t)(K + 127) / 128 : (size_t)K / 32; }
 
 static size_t fragment_index(int dtype, int K, int r, int c) {
@@ -62,6 +65,14 @@ static size_t fragment_index(int dtype, int K, int r, int c) {
   const size_t tile = (size_t)(r / 16) * ksteps(dtype, K) + (size_t)(c / KS);
   const int g = (c % KS) / (KS / 4);
   return tile * 64 + (size_t)(16 * g + r % 16);
+}
+
+/* Byte offset of the scale of MXFP4 element (r, c) inside its matrix's scales. */
+static size_t scale_index(int K, int r, int c) {
+  const size_t nblocks = (ksteps(ORA_MXFP4, K) + 15) / 16;
+  const size_t step = (size_t)(c / 128);
+  const int f = 16 * ((c % 128) / 32) + r % 16;
+  return ((size_t)(r / 16) * nblocks + step / 16) * 1024 + (size_t)(16 * f) + step % 16;
 }
 
 /* Element (r, c) of a rows x K matrix: f32 row-major; bf16 and MXFP4 tiled as
@@ -82,7 +93,7 @@ static double element(int dtype, const uint8_t* p, const uint8_t* s, int K, int 
     const int e = c % 32; /* element inside its block */
     const uint8_t byte = p[16 * f + (size_t)(e / 2)];
     const uint8_t code = (e % 2 == 0) ? (uint8_t)(byte & 0x0Fu) : (uint8_t)(byte >> 4);
-    return ora_e2m1_value(code) * ora_e8m0_value(s[f]);
+    return ora_e2m1_value(code) * ora_e8m0_value(s[scale_index(K, r, c)]);
   }
 }
 
@@ -92,7 +103,9 @@ static size_t matrix_bytes(int dtype, int rows, int K) {
   if (dtype == ORA_BF16) return (size_t)2 * rows * K;
   return (size_t)(rows / 16) * ksteps(dtype, K) * 1024;
 }
-static size_t scale_bytes(int rows, int K) { return (size_t)(rows / 16) * ksteps(ORA_MXFP4, K) * 64; }
+static size_t scale_bytes(int rows, int K) {
+  return (size_t)(rows / 16) * ((ksteps(ORA_MXFP4, K) + 15) / 16) * 1024;
+}
 
 size_t ora_expert_bytes(int dtype, int H, int I) {
   if (H <= 0 || I <= 0) return 0;

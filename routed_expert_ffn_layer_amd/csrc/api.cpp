@@ -89,9 +89,11 @@ size_t moe_expert_bytes(int wdt, int H, int I) {
     case MOE_BF16: return (H % 32 || I % 32) ? 0 : (size_t)2 * 3 * H * I;
     case MOE_MXFP4: {
       if (H % 32 || I % 32) return 0;
-      // tiled: 1 KB of codes and 64 B of scales per 16-row x 128-column tile, K padded to 128
-      const size_t t13 = (size_t)(2 * I / 16) * ((H + 127) / 128), t2 = (size_t)(H / 16) * ((I + 127) / 128);
-      return (t13 + t2) * (1024 + 64);
+      // tiled: 1 KB of codes per 16-row x 128-column tile (K padded to 128), and per
+      // row tile one 1 KB scale block per 16 column steps
+      const size_t k13 = (H + 127) / 128, k2 = (I + 127) / 128;
+      const size_t r13 = 2 * I / 16, r2 = H / 16;
+      return (r13 * k13 + r2 * k2) * 1024 + (r13 * ((k13 + 15) / 16) + r2 * ((k2 + 15) / 16)) * 1024;
     }
     default: return 0;
   }

@@ -98,15 +98,38 @@ __global__ __launch_bounds__(256) void down_f32(FfnArgs a, int shared_tiles, int
 // ===========================================================================
 // bf16 / MXFP4 weights on bf16 MFMA.
 // ===========================================================================
+// Register budget of the decode kernels.  A weight-streaming kernel needs many
+// waves' loads in flight; MXFP4 kernels are compiled for at least
+// MOE_DEC_MX1_WAVES (one token tile) or MOE_DEC_MXN_WAVES (more) waves per SIMD,
+// with their chunks shortened by MOE_DEC_MX1_DIV / MOE_DEC_MXN_DIV to fit.
 #ifndef MOE_UNROLL_SCALE
 #define MOE_UNROLL_SCALE 1
 #endif
+#ifndef MOE_DEC_MX1_WAVES
+#define MOE_DEC_MX1_WAVES 2
+#endif
+#ifndef MOE_DEC_MX1_DIV
+#define MOE_DEC_MX1_DIV 2
+#endif
+#ifndef MOE_DEC_MXN_WAVES
+#define MOE_DEC_MXN_WAVES 2
+#endif
+#ifndef MOE_DEC_MXN_DIV
+#define MOE_DEC_MXN_DIV 2
+#endif
+template <int WT, int NT>
+struct DecTune {
+  static constexpr bool mx = WT == W_MXFP4, mx1 = mx && NT == 1;
+  static constexpr int waves = mx1 ? MOE_DEC_MX1_WAVES : mx ? MOE_DEC_MXN_WAVES : 1;
+  static constexpr int div = mx1 ? MOE_DEC_MX1_DIV : mx ? MOE_DEC_MXN_DIV : 1;
+};
 // k steps per chunk of loads (bounded by the registers two chunks take).
 template <int WT, int NT, int R>
 struct Unroll {
   static constexpr int raw = WT == W_MXFP4 ? (4 / (NT * R) > 0 ? 4 / (NT * R) : 1)
                                            : (8 / (NT * R) > 0 ? 8 / (NT * R) : 1);
-  static constexpr int value = MOE_UNROLL_SCALE * (raw > 4 ? 4 : raw);
+  static constexpr int scaled = MOE_UNROLL_SCALE * (raw > 4 ? 4 : raw) / DecTune<WT, NT>::div;
+  static constexpr int value = scaled > 0 ? scaled : 1;
 };
 
 // Raw fragments of one chunk of U k steps: R weight rows (A) per step and the
@@ -129,7 +152,7 @@ struct Chunk {
 // re-read step s1-1 (never computed) and MXFP4 column groups past K (zero codes
 // in the padded tile) re-read the row's last 8 values, so every access stays in
 // its buffer.
-template <int WT, int NT, int R, int U, bool CLAMP>
+template <int WT, int NT, int R, int U, bool CLAMP, bool SCALES = true>
 __device__ __forceinline__ void load_chunk(Chunk<WT, NT, R, U>& c, const Mat& w, const int (&atile)[R], int s,
                                            int s1, int g, const Rows& rows, const int (&brow)[NT], int ntl) {
   constexpr int KS = KStep<WT>::value;
@@ -142,8 +165,8 @@ __device__ __forceinline__ void load_chunk(Chunk<WT, NT, R, U>& c, const Mat& w,
     for (int u = 0; u < U; ++u) {
       const int du = CLAMP ? min(s + u, s1 - 1) - s : u;
       c.qa[u][t] = bld16(w.codes, lane * 16, (tile_step + du) * 1024);
-      if constexpr (WT == W_MXFP4)
-        c.qs[u][t] = load_scale_word(w.scales, lane, (tile_step + du) * 64);
+      if constexpr (WT == W_MXFP4 && SCALES)
+        c.qs[u][t] = load_scale_word(w, lane, atile[t], s + du);
       else
         c.qs[u][t] = 0u;
     }
@@ -170,21 +193,24 @@ __device__ __forceinline__ void load_chunk(Chunk<WT, NT, R, U>& c, const Mat& w,
   }
 }
 
-template <int WT, int NT, int R, int U>
+// MFMAs of one chunk.  MXFP4 scales come from the chunk's per-step words, or,
+// with a scale block `sb` (16 steps per row tile, this lane's 16 bytes), from
+// byte sofs + u of it (sofs = the chunk's first step inside the block).
+template <int WT, int NT, int R, int U, bool BLOCK = false>
 __device__ __forceinline__ void compute_chunk(const Chunk<WT, NT, R, U>& c, int s, int s1, int ntl,
-                                              f32x4 (&acc)[R][NT]) {
+                                              f32x4 (&acc)[R][NT], const u32x4* sb = nullptr, int sofs = 0) {
   constexpr int NA = Chunk<WT, NT, R, U>::NA;
-  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (s + u < s1) {
+    if (BLOCK || s + u < s1) {
 #pragma unroll
       for (int t = 0; t < R; ++t) {
         bf16x8 A[NA];
         if constexpr (WT == W_BF16) {
           A[0] = as_bf16x8(c.qa[u][t]);
         } else {
-          const float sc = scale_of_word(c.qs[u][t], lane);
+          const float sc = BLOCK ? scale_of_word(sb[t][((sofs + u) % 16) / 4], sofs + u)
+                                 : scale_of_word(c.qs[u][t], s + u);
 #pragma unroll
           for (int m = 0; m < 4; ++m) A[m] = fp4x8_to_bf16x8(c.qa[u][t][m], sc);
         }
@@ -214,6 +240,41 @@ __device__ __forceinline__ void mfma_rows(const Mat& w, const int (&atile)[R], i
   constexpr int U = Unroll<WT, NT, R>::value;
   if (s0 >= s1) return;
   Chunk<WT, NT, R, U> c0, c1;
+  if constexpr (WT == W_MXFP4) {
+    // Whole 16-step scale blocks: one 16-byte scale load per lane and row tile
+    // per block, issued a block ahead (two register sets, so the unrolled body
+    // picks scale bytes at fixed positions); every load is unconditional (the
+    // chunk past the end re-reads the last one, the block past the end the last
+    // block).
+    static_assert(16 % (2 * U) == 0, "chunk pairs tile a scale block");
+    if (s0 % 16 == 0 && (s1 - s0) % 16 == 0 && w.K % 128 == 0) {
+      const int lane = threadIdx.x & 63;
+      const int nb = (s1 - s0) / 16;
+      u32x4 sb[2][R];
+      auto load_sb = [&](u32x4(&dst)[R], int step) {
+#pragma unroll
+        for (int t = 0; t < R; ++t) dst[t] = load_scale_block(w, lane, atile[t], step);
+      };
+      auto block = [&](u32x4(&cur)[R], u32x4(&next)[R], int sblk) {
+        load_sb(next, min(sblk + 16, s1 - 16));
+#pragma unroll
+        for (int i = 0; i < 16 / (2 * U); ++i) {
+          const int s = sblk + 2 * U * i;
+          load_chunk<WT, NT, R, U, false, false>(c1, w, atile, s + U, s1, g, rows, brow, ntl);
+          compute_chunk<WT, NT, R, U, true>(c0, s, s1, ntl, acc, cur, 2 * U * i);
+          load_chunk<WT, NT, R, U, false, false>(c0, w, atile, min(s + 2 * U, s1 - U), s1, g, rows, brow, ntl);
+          compute_chunk<WT, NT, R, U, true>(c1, s + U, s1, ntl, acc, cur, 2 * U * i + U);
+        }
+      };
+      load_sb(sb[0], s0);
+      load_chunk<WT, NT, R, U, false, false>(c0, w, atile, s0, s1, g, rows, brow, ntl);
+      for (int b = 0; b < nb; b += 2) {
+        block(sb[0], sb[1], s0 + 16 * b);
+        if (b + 1 < nb) block(sb[1], sb[0], s0 + 16 * (b + 1));
+      }
+      return;
+    }
+  }
   if ((s1 - s0) % (2 * U) == 0 && (WT != W_MXFP4 || w.K % 128 == 0)) {
     load_chunk<WT, NT, R, U, false>(c0, w, atile, s0, s1, g, rows, brow, ntl);
     for (int s = s0; s < s1; s += 2 * U) {
@@ -242,7 +303,8 @@ __device__ __forceinline__ void mfma_rows(const Mat& w, const int (&atile)[R], i
 // 16-row A tile = gate rows j..j+7 stacked on up rows j..j+7, so the epilogue
 // pairs lane l (gate) with lane l+32 (up) and writes h = SiLU(gate) * up as bf16.
 template <int WT, int NT, int KW, int R>
-__global__ __launch_bounds__(256) void gate_up_mfma(FfnArgs a, int shared_tiles, int routed_tiles) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT, NT>::waves))) void gate_up_mfma(
+    FfnArgs a, int shared_tiles, int routed_tiles) {
   constexpr int RT = 4 / KW;
   const Item it = resolve_item(a, shared_tiles, routed_tiles);
   if (!it.valid) return;
@@ -337,7 +399,8 @@ __global__ __launch_bounds__(256) void gate_up_mfma(FfnArgs a, int shared_tiles,
 
 // down: row tile t of a wave is 16 output columns (rows of W2) of one item.
 template <int WT, int NT, int KW, int R>
-__global__ __launch_bounds__(256) void down_mfma(FfnArgs a, int shared_tiles, int routed_tiles) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT, NT>::waves))) void down_mfma(
+    FfnArgs a, int shared_tiles, int routed_tiles) {
   constexpr int RT = 4 / KW;
   const Item it = resolve_item(a, shared_tiles, routed_tiles);
   if (!it.valid) return;
@@ -437,25 +500,29 @@ size_t ffn_workspace_bytes(int wtype, int T, int k, int I, int I_shared) {
 struct Shape {
   int kw, r;
 };
+#ifndef MOE_DEC_MXN_R
+#define MOE_DEC_MXN_R 4
+#endif
 static Shape gate_up_shape(int wtype, int T) {
   if (wtype == W_BF16) return T <= 4 ? Shape{4, 1} : Shape{2, 1};
-  return T <= 16 ? Shape{1, 2} : Shape{1, 4};
+  return T <= 16 ? Shape{1, 2} : Shape{1, MOE_DEC_MXN_R};
 }
 static Shape down_shape(int wtype, int T) {
   if (wtype == W_BF16) return Shape{1, 2};
-  return T <= 16 ? Shape{1, 2} : Shape{1, 4};
+  return T <= 16 ? Shape{1, 2} : Shape{1, MOE_DEC_MXN_R};
 }
 
-static int pick_nt(int T) {
-  if (T <= 16) return 1;
-  if (T <= 32) return 2;
-  if (T <= 64) return 4;
-  return 8;
+#ifndef MOE_DEC_MX_NTMAX
+#define MOE_DEC_MX_NTMAX 2
+#endif
+static int pick_nt(int T, int wtype) {
+  const int nt = T <= 16 ? 1 : T <= 32 ? 2 : T <= 64 ? 4 : 8;
+  return wtype == W_MXFP4 && nt > MOE_DEC_MX_NTMAX ? MOE_DEC_MX_NTMAX : nt;
 }
 
 template <int WT, int KW, int R>
 static void gu_nt(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int rt) {
-  switch (pick_nt(a.T)) {
+  switch (pick_nt(a.T, WT)) {
     case 1: launch_ffn_kernel(gate_up_mfma<WT, 1, KW, R>, grid, st, a, sh, rt); break;
     case 2: launch_ffn_kernel(gate_up_mfma<WT, 2, KW, R>, grid, st, a, sh, rt); break;
     case 4: launch_ffn_kernel(gate_up_mfma<WT, 4, KW, R>, grid, st, a, sh, rt); break;
@@ -464,7 +531,7 @@ static void gu_nt(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int r
 }
 template <int WT, int KW, int R>
 static void dn_nt(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int rt) {
-  switch (pick_nt(a.T)) {
+  switch (pick_nt(a.T, WT)) {
     case 1: launch_ffn_kernel(down_mfma<WT, 1, KW, R>, grid, st, a, sh, rt); break;
     case 2: launch_ffn_kernel(down_mfma<WT, 2, KW, R>, grid, st, a, sh, rt); break;
     case 4: launch_ffn_kernel(down_mfma<WT, 4, KW, R>, grid, st, a, sh, rt); break;

@@ -61,16 +61,15 @@ struct KStep {
   static constexpr int value = WT == W_MXFP4 ? 128 : 32;
 };
 
-// k steps whose loads are issued together before any of their MFMAs (bounded by
-// the registers the raw A and B fragments take).
 // One tiled weight matrix of an expert, addressed through buffer resources:
 // the uniform part of every address (tile, step) is a scalar offset and the
 // per-lane part (fragment `lane`) a fixed vector offset, so a load costs no
 // vector ALU work.
 struct Mat {
   __amdgpu_buffer_rsrc_t codes;   // 1 KB per (row tile, column step)
-  __amdgpu_buffer_rsrc_t scales;  // MXFP4: 64 B per (row tile, column step)
+  __amdgpu_buffer_rsrc_t scales;  // MXFP4: 1 KB per (row tile, 16 column steps)
   int nK;                         // column steps
+  int nKs;                        // MXFP4 scale blocks per row tile (16 steps each)
   int K;                          // columns
 };
 
@@ -92,15 +91,26 @@ __device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int voff, int s
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// Block scale of this lane's MXFP4 fragment.  A tile's 64 scale bytes are read
-// as 16 words, each lane loading the word that holds its byte; the byte is only
-// picked out where the scale is used, so the wait for the load stays there too
-// (a byte load is widened right after it is issued, which forces an early wait).
-__device__ __forceinline__ uint32_t load_scale_word(__amdgpu_buffer_rsrc_t r, int lane, int soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, lane & ~3, soff, 0);
+// MXFP4 block scales.  Per row tile the column steps form blocks of 16; in the
+// 1 KB scale block of (row tile, step / 16) this lane's fragment owns bytes
+// 16 * lane .. 16 * lane + 15, byte i being its scale at step 16 * block + i.
+// A lane reads the whole 16 bytes at once (16 steps), or the word holding 4 of
+// them; the byte is only picked out where the scale is used, so the wait for the
+// load stays there too (a byte load is widened right after it is issued, which
+// forces an early wait).
+__device__ __forceinline__ int scale_block_offset(const Mat& w, int tile, int step) {
+  return (tile * w.nKs + step / 16) * 1024;
 }
-__device__ __forceinline__ float scale_of_word(uint32_t word, int lane) {
-  return e8m0_to_f32((word >> (8 * (lane & 3))) & 0xffu);
+__device__ __forceinline__ u32x4 load_scale_block(const Mat& w, int lane, int tile, int step) {
+  return bld16(w.scales, lane * 16, scale_block_offset(w, tile, step));
+}
+__device__ __forceinline__ uint32_t load_scale_word(const Mat& w, int lane, int tile, int step) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(w.scales, lane * 16,
+                                                         scale_block_offset(w, tile, step) + (step % 16) / 4 * 4, 0);
+}
+// The scale of step `step` from the word holding it.
+__device__ __forceinline__ float scale_of_word(uint32_t word, int step) {
+  return e8m0_to_f32((word >> (8 * (step & 3))) & 0xffu);
 }
 
 // Column steps of a K-wide matrix and byte offsets inside an expert slot.
@@ -108,23 +118,30 @@ template <int WT>
 __device__ __forceinline__ int ksteps(int K) {
   return WT == W_MXFP4 ? (K + 127) / 128 : K / 32;
 }
+// Slot: codes of W13 (2*Ie rows, K = H), codes of W2 (H rows, K = Ie), then for
+// MXFP4 the scale blocks of W13 and of W2.
 template <int WT>
 __device__ __forceinline__ Mat w13_mat(const uint8_t* slot, int H, int Ie) {
-  const size_t t13 = (size_t)(2 * Ie / 16) * ksteps<WT>(H), t2 = (size_t)(H / 16) * ksteps<WT>(Ie);
+  const size_t r13 = 2 * Ie / 16, r2 = H / 16, k13 = ksteps<WT>(H), k2 = ksteps<WT>(Ie);
+  const size_t c13 = r13 * k13 * 1024, c2 = r2 * k2 * 1024;
   Mat m;
-  m.codes = make_rsrc(slot, t13 * 1024);
-  m.scales = make_rsrc(WT == W_MXFP4 ? slot + (t13 + t2) * 1024 : slot, WT == W_MXFP4 ? t13 * 64 : 0);
-  m.nK = ksteps<WT>(H);
+  m.codes = make_rsrc(slot, c13);
+  m.nKs = (int)((k13 + 15) / 16);
+  m.scales = make_rsrc(WT == W_MXFP4 ? slot + c13 + c2 : slot, WT == W_MXFP4 ? r13 * m.nKs * 1024 : 0);
+  m.nK = (int)k13;
   m.K = H;
   return m;
 }
 template <int WT>
 __device__ __forceinline__ Mat w2_mat(const uint8_t* slot, int H, int Ie) {
-  const size_t t13 = (size_t)(2 * Ie / 16) * ksteps<WT>(H), t2 = (size_t)(H / 16) * ksteps<WT>(Ie);
+  const size_t r13 = 2 * Ie / 16, r2 = H / 16, k13 = ksteps<WT>(H), k2 = ksteps<WT>(Ie);
+  const size_t c13 = r13 * k13 * 1024, c2 = r2 * k2 * 1024;
+  const size_t s13 = r13 * ((k13 + 15) / 16) * 1024;
   Mat m;
-  m.codes = make_rsrc(slot + t13 * 1024, t2 * 1024);
-  m.scales = make_rsrc(WT == W_MXFP4 ? slot + (t13 + t2) * 1024 + t13 * 64 : slot, WT == W_MXFP4 ? t2 * 64 : 0);
-  m.nK = ksteps<WT>(Ie);
+  m.codes = make_rsrc(slot + c13, c2);
+  m.nKs = (int)((k2 + 15) / 16);
+  m.scales = make_rsrc(WT == W_MXFP4 ? slot + c13 + c2 + s13 : slot, WT == W_MXFP4 ? r2 * m.nKs * 1024 : 0);
+  m.nK = (int)k2;
   m.K = Ie;
   return m;
 }

@@ -57,7 +57,7 @@ __device__ __forceinline__ void load_a(AChunk<WT, R, U>& c, const Mat& w, const 
     for (int u = 0; u < U; ++u) {
       c.qa[u][t] = bld16(w.codes, lane * 16, (ts + u) * 1024);
       if constexpr (WT == W_MXFP4)
-        c.qs[u][t] = load_scale_word(w.scales, lane, (ts + u) * 64);
+        c.qs[u][t] = load_scale_word(w, lane, atile[t], s + u);
       else
         c.qs[u][t] = 0u;
     }
@@ -102,11 +102,10 @@ __device__ __forceinline__ int b_frag_offset(int q) {
 // R*NTL MFMAs; consecutive MFMAs update different accumulators.
 template <int WT, int NTL, int R, int U>
 __device__ __forceinline__ void compute_chunk_lds(const AChunk<WT, R, U>& c, const uint8_t* buf,
-                                                  const int (&boff)[4], f32x4 (&acc)[R][NTL]) {
+                                                  const int (&boff)[4], int step4, f32x4 (&acc)[R][NTL]) {
   constexpr int NA = WT == W_MXFP4 ? 4 : 1;
   constexpr int NG = U * NA;  // k-groups of 32 columns in the chunk
   static_assert(NG == 4, "a chunk is four k-groups");
-  const int lane = threadIdx.x & 63;
   auto ldb = [&](int q, int nt) {
     return as_bf16x8(*reinterpret_cast<const u32x4*>(buf + boff[q] + nt * 16 * kPfRowBytes));
   };
@@ -121,7 +120,7 @@ __device__ __forceinline__ void compute_chunk_lds(const AChunk<WT, R, U>& c, con
       if constexpr (WT == W_BF16) {
         A[t][0] = as_bf16x8(c.qa[u][t]);
       } else {
-        const float sc = scale_of_word(c.qs[u][t], lane);
+        const float sc = scale_of_word(c.qs[u][t], step4 + u);
 #pragma unroll
         for (int m = 0; m < 4; ++m) A[t][m] = fp4x8_to_bf16x8(c.qa[u][t][m], sc);
       }
@@ -207,7 +206,7 @@ __device__ __forceinline__ void prefill_units(const Mat& w, int nu, const ATileO
   vm_lds_barrier<2 * NL>();
   auto step = [&](int d, int f) {
     issue((d + kPfDepth - 1) % kPfDepth, min(f + kPfDepth - 1, lastf));
-    compute_chunk_lds<WT, NTL, R, U>(a[d], bufs.b[d], boff, acc);
+    compute_chunk_lds<WT, NTL, R, U>(a[d], bufs.b[d], boff, d, acc);  // chunk index = d mod 4
     vm_lds_barrier<2 * NL>();
   };
   if (nchunks % kPfDepth == 0) {

@@ -107,8 +107,13 @@ def _matrix_bytes(dtype, rows, K):
     return rows // 16 * _ksteps(dtype, K) * 1024
 
 
+def _scale_blocks(K):
+    """16-step blocks of MXFP4 scales per row tile."""
+    return -(-_ksteps(MXFP4, K) // 16)
+
+
 def _scale_bytes(rows, K):
-    return rows // 16 * _ksteps(MXFP4, K) * 64
+    return rows // 16 * _scale_blocks(K) * 1024
 
 
 def slot_offsets(dtype: int, H: int, I: int) -> dict:
@@ -146,7 +151,12 @@ def _tile_mx(m):
     pad_s = np.zeros((R, nk * 4), np.uint8)
     pad_s[:, : K // 32] = scales
     tc = pad_c.reshape(R // 16, 16, nk, 4, 16).transpose(0, 2, 3, 1, 4).ravel()
-    ts = pad_s.reshape(R // 16, 16, nk, 4).transpose(0, 2, 3, 1).ravel()
+    # scales: per row tile, blocks of 16 column steps; inside a block fragment
+    # f = 16*group + row%16 owns 16 bytes, byte i = its scale at step 16*block + i
+    nb = _scale_blocks(K)
+    pad_s2 = np.zeros((R, nb * 16 * 4), np.uint8)
+    pad_s2[:, : nk * 4] = pad_s
+    ts = pad_s2.reshape(R // 16, 16, nb, 16, 4).transpose(0, 2, 4, 1, 3).ravel()
     return tc, ts
 
 
@@ -249,23 +259,32 @@ def torch_mxfp4_expert_pool(n_experts: int, H: int, I: int, seed: int, device, s
     """uint8 tensor [n_experts][expert_bytes] of MXFP4 experts with N(0, std) weights.
 
     Every element is an independent draw, so consecutive 32-element blocks of the
-    flat draw vector can be placed at consecutive fragments of the tiled layout;
-    codes and scales are written in the same fragment order, so each scale sits
-    with its own block.  Experts are drawn `chunk` at a time.
+    flat draw vector can be placed at consecutive fragments of the tiled layout
+    (fragment order: matrix, row tile, column step, fragment); each scale is then
+    moved from that order to its place in the blocked scale layout.  Experts are
+    drawn `chunk` at a time.
     """
     import torch
-    assert H % 128 == 0 and I % 128 == 0, "bulk MXFP4 pools need K multiples of 128 (no padding)"
+    assert H % 2048 == 0 and I % 2048 == 0, "bulk MXFP4 pools need 16-step multiples of K (no padding)"
     nb = expert_bytes(MXFP4, H, I)
     n = 3 * H * I
+    mats = [(2 * I, H), (H, I)]  # W13, W2: (rows, K)
     out = torch.empty((n_experts, nb), dtype=torch.uint8, device=device)
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     for e0 in range(0, n_experts, chunk):
         e1 = min(n_experts, e0 + chunk)
-        w = torch.randn((e1 - e0) * n, generator=g, device=device, dtype=torch.float32) * std
+        ne = e1 - e0
+        w = torch.randn(ne * n, generator=g, device=device, dtype=torch.float32) * std
         c, s = torch_mx_quantize_flat(w)
-        c = c.view(e1 - e0, n // 2)
-        s = s.view(e1 - e0, n // 32)
-        out[e0:e1, : n // 2].copy_(c)
-        out[e0:e1, n // 2:].copy_(s)
+        out[e0:e1, : n // 2].copy_(c.view(ne, n // 2))
+        s = s.view(ne, n // 32)
+        pos, off = n // 2, 0
+        for rows, K in mats:
+            rt, nk = rows // 16, K // 128
+            cnt = rt * nk * 64
+            blk = s[:, off:off + cnt].reshape(ne, rt, nk // 16, 16, 64).transpose(3, 4)
+            out[e0:e1, pos:pos + cnt].copy_(blk.reshape(ne, cnt))
+            pos += cnt
+            off += cnt
     return out

@@ -124,6 +124,12 @@ SMALL = [
     (synth.BF16, 300, 384, 128, 4, 2, True),
     (synth.MXFP4, 600, 512, 256, 16, 4, True),
     (synth.MXFP4, 257, 256, 384, 8, 1, False),
+    # MXFP4 decode with whole 16-step scale blocks (K = 2048): one and two token
+    # tiles, a shared expert whose down K (1024) is half a block, and 40 tokens per
+    # expert (two passes of at most 32)
+    (synth.MXFP4, 24, 2048, 2048, 4, 2, False),
+    (synth.MXFP4, 6, 2048, 2048, 3, 2, True),
+    (synth.MXFP4, 40, 2048, 2048, 2, 2, False),
 ]
 
 

@@ -60,30 +60,41 @@ def _frag(row, k, K, KS):
     return ((row // 16) * nk + k // KS) * 64 + 16 * ((k % KS) // (KS // 4)) + row % 16
 
 
+def _scale_pos(row, k, K):
+    """Byte of the scale of MXFP4 element (row, k), written out from the layout
+    description: per row tile, 1 KB blocks of 16 column steps; fragment f owns 16
+    bytes of a block, byte i being its scale at step 16*block + i."""
+    nk = -(-K // 128)
+    nblocks = -(-nk // 16)
+    step = k // 128
+    f = 16 * ((k % 128) // 32) + row % 16
+    return ((row // 16) * nblocks + step // 16) * 1024 + 16 * f + step % 16
+
+
 def test_mxfp4_slot_layout_hand_built(ora):
     """A slot assembled byte by byte from the layout description decodes as intended.
 
     H = I = 32: W13 has 64 stored rows (4 tiles x 1 padded step), W2 32 rows (2 tiles);
-    codes 4096 + 2048 bytes, scales 256 + 128 bytes.  Stored W13 row 16t+q is gate
-    row 8t+q for q < 8, up row 8t+q-8 otherwise.
+    codes 4096 + 2048 bytes, scales 4 + 2 blocks of 1 KB.  Stored W13 row 16t+q is
+    gate row 8t+q for q < 8, up row 8t+q-8 otherwise.
     """
     H = I = 32
     nbytes = ora.expert_bytes(ora.MXFP4, H, I)
-    assert nbytes == 4096 + 2048 + 256 + 128
-    c13, c2, s13, s2 = 0, 4096, 6144, 6400
+    assert nbytes == 4096 + 2048 + 4096 + 2048
+    c13, c2, s13, s2 = 0, 4096, 6144, 10240
     slot = np.zeros(nbytes, np.uint8)
-    slot[s13:s13 + 256] = 127      # scale 1.0 everywhere (padding fragments included)
-    slot[s2:s2 + 128] = 127
+    slot[s13:s13 + 4096] = 127     # scale 1.0 everywhere (padding included)
+    slot[s2:s2 + 2048] = 127
     f = _frag(0, 0, H, 128)          # gate row 0 -> stored row 0; elements 0, 1
     slot[c13 + 16 * f] = 0x21        # elem 0 = code 1 (0.5), elem 1 = code 2 (1.0)
     f = _frag(8, 6, H, 128)          # up row 0 -> stored row 8; elements 6, 7 in byte 3
     slot[c13 + 16 * f + 3] = 0x9F    # elem 6 = code 15 (-6), elem 7 = code 9 (-0.5)
-    slot[s13 + f] = 129              # scale 4
+    slot[s13 + _scale_pos(8, 6, H)] = 129   # scale 4
     f = _frag(16 + 1, 5, H, 128)     # gate row 9 -> stored row 17; element 5 = high nibble of byte 2
     slot[c13 + 16 * f + 2] = 0x50    # code 5 (3.0)
     f = _frag(5, 31, I, 128)         # down row 5, element 31 = high nibble of byte 15
     slot[c2 + 16 * f + 15] = 0x70    # code 7 (6.0)
-    slot[s2 + f] = 126               # scale 0.5
+    slot[s2 + _scale_pos(5, 31, I)] = 126   # scale 0.5
     wg, wu, wd = ora.decode_expert(ora.MXFP4, slot, H, I)
     exp_g = np.zeros((I, H)); exp_g[0, 0] = 0.5; exp_g[0, 1] = 1.0; exp_g[9, 5] = 3.0
     exp_u = np.zeros((I, H)); exp_u[0, 6] = -24.0; exp_u[0, 7] = -2.0
@@ -130,15 +141,41 @@ def test_f32_slot_layout_hand_built(ora):
 def test_mxfp4_padding_for_k_not_multiple_of_128(ora):
     H, I = 160, 96   # K = 160 -> 2 steps (96 padded columns); K = 96 -> 1 step (32 padded)
     nb = ora.expert_bytes(ora.MXFP4, H, I)
-    assert nb == (2 * I // 16) * 2 * 1024 + (H // 16) * 1 * 1024 + (2 * I // 16) * 2 * 64 + (H // 16) * 64
+    # codes: 2 steps and 1 step of 1 KB per row tile; scales: one 1 KB block per row tile
+    assert nb == (2 * I // 16) * 2 * 1024 + (H // 16) * 1 * 1024 + (2 * I // 16) * 1024 + (H // 16) * 1024
     assert nb == synth.expert_bytes(synth.MXFP4, H, I)
+
+
+def test_mxfp4_scales_past_sixteen_steps(ora):
+    """K = 17 * 128: each row tile holds two scale blocks, the second with one used
+    step; a scale written at step 16 (block 1, byte 0) and one at step 15 (block 0,
+    byte 15) land on their own elements only."""
+    H, I = 17 * 128, 32
+    nb = ora.expert_bytes(ora.MXFP4, H, I)
+    c13 = 0
+    s13 = (2 * I // 16) * 17 * 1024 + (H // 16) * 1 * 1024
+    assert nb == s13 + (2 * I // 16) * 2 * 1024 + (H // 16) * 1024
+    slot = np.zeros(nb, np.uint8)
+    slot[s13:] = 127
+    for row, k, code, sc in ((0, 16 * 128 + 3, 0x02, 130), (3, 15 * 128 + 64, 0x01, 125)):
+        f = _frag(row, k, H, 128)
+        e = k % 32
+        slot[c13 + 16 * f + e // 2] |= code << (4 * (e % 2))
+        slot[s13 + _scale_pos(row, k, H)] = sc
+    wg, wu, wd = ora.decode_expert(ora.MXFP4, slot, H, I)
+    exp_g = np.zeros((I, H))
+    exp_g[0, 16 * 128 + 3] = 1.0 * 8.0     # code 2 (1.0) x 2^3
+    exp_g[3, 15 * 128 + 64] = 0.5 * 0.25   # code 1 (0.5) x 2^-2
+    np.testing.assert_array_equal(wg, exp_g)
+    np.testing.assert_array_equal(wu, np.zeros((I, H)))
+    np.testing.assert_array_equal(wd, np.zeros((H, I)))
 
 
 def test_mxfp4_roundtrip_of_representable_values(ora):
     """Values c * 2^e with c an E2M1 value and a block max of 6 * 2^e survive the
     generator's encoding and the oracle's decoding exactly."""
     g = np.random.default_rng(3)
-    H, I = 64, 32
+    H, I = 17 * 128, 96   # W13 rows span two scale blocks (the second partly padding)
     mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
 
     def mat(rows, K):
