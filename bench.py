@@ -37,9 +37,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "MoE-layer tokens/s at 1 MI355X; % HBM BW (decode), % MFMA peak (prefill)"
-COUNTERS = os.path.join(ROOT, "profiles", "gate_up_mfma_bf16_decode_T16_counters.txt")
+# HBM byte counters of each workload's dominant kernel (rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs summarised by --summarize-counters), valid while the FFN
+# sources hash to the value recorded in the file.
+COUNTERS = {
+    "decode_bf16": ("gate_up_mfma_bf16_decode_T16_counters.txt", "gate_up_mfma"),
+    "decode_mxfp4": ("gate_up_mfma_mxfp4_decode_T64_counters.txt", "gate_up_mfma"),
+    "prefill_mxfp4": ("prefill_gate_up_mxfp4_T4096_counters.txt", "prefill_gate_up"),
+}
 FFN_SOURCES = [os.path.join(ROOT, "routed_expert_ffn_layer_amd", "csrc", f)
-               for f in ("ffn.hip", "ffn_common.hpp", "common.hpp")]
+               for f in ("ffn.hip", "ffn_prefill.hip", "ffn_common.hpp", "common.hpp")]
 WORKLOADS = ("decode_bf16", "decode_mxfp4", "prefill_mxfp4", "cached_trace_bf16", "hostbw")
 
 
@@ -60,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--summarize-counters", metavar="PROF_DIR", default=None,
+                    help="print per-kernel HBM bytes per dispatch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs (no GPU)")
     return ap.parse_args()
 
 
@@ -75,16 +84,62 @@ def ffn_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per gate_up launch from the committed counter summary (rocprofv3
-    FETCH_SIZE + WRITE_SIZE, scaled by the same counters on a copy of known size),
-    or None if the kernel source changed since the counters were taken."""
-    if not os.path.exists(COUNTERS):
+def measured_traffic(workload):
+    """HBM bytes per launch of the workload's dominant kernel from the committed
+    counter summary (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by the same counters
+    on a copy of known size), or None if there is none or the kernel sources
+    changed since the counters were taken."""
+    if workload not in COUNTERS:
         return None
-    d = json.loads("\n".join(l for l in open(COUNTERS).read().splitlines() if not l.startswith("#")))
+    path = os.path.join(ROOT, "profiles", COUNTERS[workload][0])
+    if not os.path.exists(path):
+        return None
+    d = json.loads("\n".join(l for l in open(path).read().splitlines() if not l.startswith("#")))
     if d.get("ffn_source_sha256") != ffn_source_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    k = d.get("kernels", {}).get(COUNTERS[workload][1])
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def summarize_counters(prof_dir):
+    """Per-kernel HBM bytes per dispatch from rocprofv3 --pmc runs laid out as
+    prof_dir/{FETCH_SIZE,WRITE_SIZE}/**.csv (the workload) and
+    prof_dir/{FETCH_SIZE,WRITE_SIZE}_copy/**.csv (bench.py --calibrate-copy).
+    Counters are KiB per dispatch; each is scaled by bytes/KiB read on the copy."""
+    import csv
+    import glob
+    import re
+
+    def load(sub):
+        per = {}
+        for f in glob.glob(os.path.join(prof_dir, sub, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                name = re.sub(r"^void ", "", r["Kernel_Name"]).split("(")[0].split("<")[0].split("::")[-1]
+                d = per.setdefault(name, {"sum": 0.0, "dispatches": set()})
+                d["sum"] += float(r["Counter_Value"])
+                d["dispatches"].add(r.get("Dispatch_Id", r.get("Correlation_Id")))
+        return {k: (v["sum"] / len(v["dispatches"]), len(v["dispatches"])) for k, v in per.items()}
+
+    n_copy = 256 << 20
+    fc = load("FETCH_SIZE_copy")
+    wc = load("WRITE_SIZE_copy")
+    copy_kernel = max(fc, key=lambda k: fc[k][0])
+    f_factor = n_copy / (fc[copy_kernel][0] * 1024.0)
+    w_factor = n_copy / (wc[copy_kernel][0] * 1024.0)
+    fk, wk = load("FETCH_SIZE"), load("WRITE_SIZE")
+    kernels = {}
+    for k in sorted(set(fk) & set(wk)):
+        fb = fk[k][0] * 1024.0 * f_factor
+        wb = wk[k][0] * 1024.0 * w_factor
+        kernels[k] = {"fetch_kib_raw": round(fk[k][0], 1), "write_kib_raw": round(wk[k][0], 1),
+                      "fetch_bytes": int(fb), "write_bytes": int(wb), "hbm_bytes_per_launch": int(fb + wb),
+                      "dispatches": fk[k][1]}
+    return {"ffn_source_sha256": ffn_source_hash(),
+            "copy_calibration": {"copy_kernel": copy_kernel, "copy_bytes": n_copy,
+                                 "fetch_kib_raw": round(fc[copy_kernel][0], 1),
+                                 "write_kib_raw": round(wc[copy_kernel][0], 1),
+                                 "fetch_factor": round(f_factor / 1.0, 6), "write_factor": round(w_factor, 6)},
+            "kernels": kernels}
 
 
 def calibrate_copy():
@@ -276,7 +331,7 @@ def workload_decode_bf16(args):
          "tokens_per_layer": T, "stacked_layers": n_layers,
          "weights_in_hbm_gb": round(n_layers * 257 * 6291456 / 1e9, 2), "slots": "all resident"},
         {"kernel": "gate_up_mfma<bf16> (moe_grouped_ffn_gate_up)", "bound": "hbm", "achieved": achieved,
-         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("decode_bf16"),
          "avg_launch_us": main_res["gate_up_avg_us"], "algorithmic_bytes_per_launch": main_res["gate_up_bytes_avg"],
          "launches_timed": main_res["gate_up_launches_timed"],
          "timing": "events around back-to-back passes of the timed layers' gate_up launches"},
@@ -432,7 +487,8 @@ def workload_decode_mxfp4(args):
          "tokens_per_layer": T, "stacked_layers": n_layers,
          "weights_in_hbm_gb": round(stack.numel() / 1e9, 2), "slots": "all resident"},
         {"kernel": "gate_up_mfma<mxfp4> (moe_grouped_ffn_gate_up)", "bound": "hbm", "achieved": m["gate_up_gbs"],
-         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": m["gate_up_gbs"] / HBM_PEAK_GBS, "traffic": None,
+         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": m["gate_up_gbs"] / HBM_PEAK_GBS,
+         "traffic": measured_traffic("decode_mxfp4"),
          "avg_launch_us": m["gate_up_avg_us"], "algorithmic_bytes_per_launch": m["gate_up_bytes_avg"],
          "launches_timed": m["gate_up_launches_timed"],
          "timing": "events around back-to-back passes of the stack's gate_up launches"},
@@ -581,7 +637,8 @@ def workload_prefill_mxfp4(args):
          "tokens_per_layer": T, "stacked_layers": n_layers, "host_layers_distinct": n_host,
          "layer_bytes": lb, "slots": "two HBM banks, one layer each"},
         {"kernel": "prefill_gate_up<mxfp4> (moe_grouped_ffn_gate_up)", "bound": "mfma", "achieved": gu_tf,
-         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": gu_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": gu_tf / MFMA_BF16_PEAK_TFLOPS,
+         "traffic": measured_traffic("prefill_mxfp4"),
          "avg_launch_us": gu * 1e6, "algorithmic_flop_per_launch": gu_flop, "launches_timed": 10,
          "timing": "events around back-to-back gate_up launches on one layer's routing"},
         cpu,
@@ -736,6 +793,9 @@ def cpu_cached_trace(trace, host, c, n_layers, n_host, S, seconds):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer runs on a single MI355X)",
               file=sys.stderr)
