@@ -312,7 +312,7 @@ def workload_decode_bf16(args):
     T = args.tokens or 16
     n_layers = args.layers or 16
     steps, warmup = args.steps or 50, 5 if args.warmup is None else args.warmup
-    extra = [int(v) for v in (args.extra_batches or "1,4").split(",") if v.strip()]
+    extra = [int(v) for v in ("1,4" if args.extra_batches is None else args.extra_batches).split(",") if v.strip()]
     main_res = run_decode_bf16(T, n_layers, steps, warmup)
     keys = ("layer_tokens_per_s", "ms_per_step", "layer_hbm_gbs", "gate_up_gbs", "gate_up_avg_us",
             "active_experts_mean")
@@ -466,7 +466,8 @@ def workload_decode_mxfp4(args):
     n_layers = args.layers or c["layers"]
     steps, warmup = args.steps or 10, 2 if args.warmup is None else args.warmup
     T = args.tokens or 64
-    batches = [T] + [int(v) for v in (args.extra_batches or "1,8").split(",") if v.strip() and int(v) != T]
+    extra = "1,8" if args.extra_batches is None else args.extra_batches
+    batches = [T] + [int(v) for v in extra.split(",") if v.strip() and int(v) != T]
     dev = torch.device("cuda:0")
     stack, distinct = mxfp4_resident_stack(c, n_layers, args.distinct_experts, dev)
     del distinct
