@@ -184,7 +184,7 @@ int moe_cache_inject_fill_failure(moe_cache* c, int64_t n);
 
 /* ------------------------------------------------------------------------- */
 /* Grouped SwiGLU expert FFN.  The pages: GPU expert compute on cached and filled
- * experts, bit-exact with no precision relaxation ("Three mechanisms";
+ * experts, exact, with precision never lowered ("Three mechanisms";
  * "Key Takeaways").  For every expert e with counts > 0 and slot_of_expert[e] >= 0,
  * for each of its pairs p in [offsets[e], offsets[e+1]) with token t = sorted_rows[p]/k:
  *     out_rows[p] = W2 . ( SiLU(Wgate . x[t]) * (Wup . x[t]) ),   SiLU(z) = z/(1+e^-z)
@@ -218,7 +218,7 @@ int moe_grouped_ffn_down(int wdt, const void* slot_pool, size_t slot_stride, con
                          float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------- */
-/* Combine.  The pages: the partial sums merge exactly ("Three mechanisms").
+/* Combine.  The pages: the partial sums are added without approximation ("Three mechanisms").
  *   y[t] = sum_{j=0..k-1} topk_w[t][j] * out_rows[inv_rows[t*k+j]]  (+ shared_out[t])
  * in f32, j in increasing order (fused multiply-add), then the shared term,
  * then one rounding to ydt (MOE_F32, or MOE_BF16 with round-to-nearest-even).

@@ -46,7 +46,8 @@ double ora_e8m0_value(uint8_t code) {
 }
 
 /* Tiled slot layout (a reading: the pages say only that experts are stored in
- * their "final host layout", "Three mechanisms", elastic memory management).
+ * pinned host memory in the layout they are computed from, "Three mechanisms",
+ * elastic memory management).
  * A matrix of `rows` rows (a multiple of 16) and K columns is cut into tiles of
  * 16 rows by KS columns (KS = 32 for bf16, 128 for MXFP4); tiles are stored
  * row-tile major, then by column step.  Inside a tile the 64 fragments of 16
@@ -114,7 +115,7 @@ size_t ora_expert_bytes(int dtype, int H, int I) {
   return matrix_bytes(dtype, 2 * I, H) + matrix_bytes(dtype, H, I) + scale_bytes(2 * I, H) + scale_bytes(H, I);
 }
 
-/* Slot layout ("final host layout", one contiguous run per expert):
+/* Slot layout (the layout experts are kept in, host and device; one contiguous run per expert):
  *   W13 (2I rows, K = H) then W2 (H rows, K = I); MXFP4: codes of W13, codes of
  *   W2, scales of W13, scales of W2.
  * Row order of W13: f32 keeps gate rows 0..I-1 then up rows; bf16 and MXFP4
@@ -269,7 +270,7 @@ void ora_expert_ffn(const double* wg, const double* wu, const double* wd, int H,
   free(h);
 }
 
-/* The pages say the partial sums of the routed experts merge exactly ("Three
+/* The pages say the routed experts' partial sums are added without approximation ("Three
  * mechanisms"); the merge is the gate-weighted sum, plus the shared expert with
  * weight 1 when the layer has one. */
 void ora_combine(const double* rows, const double* w, const double* shared, int T, int k, int H, double* y) {

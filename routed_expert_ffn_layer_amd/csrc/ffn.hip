@@ -3,7 +3,7 @@
 // Pages: "Meet FreeToken: An Edge-Native MoE Serving Engine that Runs 753B GLM-5.2
 // on a Single Workstation GPU" (MarkTechPost).  The GPU computes the experts that
 // are resident in its cache ("Three mechanisms": bandwidth-adaptive execution),
-// with expert output bit-exact and no precision relaxation ("Key Takeaways"): MXFP4
+// with expert output exact and precision never lowered ("Key Takeaways"): MXFP4
 // weights are expanded to bf16 exactly before the bf16 MFMA.  The FFN form
 // (SwiGLU: down(SiLU(gate x) * up x)) is not on the pages; it is the standard
 // MoE expert.
@@ -500,16 +500,19 @@ size_t ffn_workspace_bytes(int wtype, int T, int k, int I, int I_shared) {
 struct Shape {
   int kw, r;
 };
+#ifndef MOE_DEC_MX1_R
+#define MOE_DEC_MX1_R 2
+#endif
 #ifndef MOE_DEC_MXN_R
 #define MOE_DEC_MXN_R 4
 #endif
 static Shape gate_up_shape(int wtype, int T) {
   if (wtype == W_BF16) return T <= 4 ? Shape{4, 1} : Shape{2, 1};
-  return T <= 16 ? Shape{1, 2} : Shape{1, MOE_DEC_MXN_R};
+  return T <= 16 ? Shape{1, MOE_DEC_MX1_R} : Shape{1, MOE_DEC_MXN_R};
 }
 static Shape down_shape(int wtype, int T) {
   if (wtype == W_BF16) return Shape{1, 2};
-  return T <= 16 ? Shape{1, 2} : Shape{1, MOE_DEC_MXN_R};
+  return T <= 16 ? Shape{1, MOE_DEC_MX1_R} : Shape{1, MOE_DEC_MXN_R};
 }
 
 #ifndef MOE_DEC_MX_NTMAX
@@ -557,7 +560,8 @@ hipError_t launch_ffn_gate_up(int wtype, const FfnArgs& a, hipStream_t st) {
     if (sp.kw == 4) gu_nt<W_BF16, 4, 1>(a, st, grid, shared_tiles, routed_tiles);
     else gu_nt<W_BF16, 2, 1>(a, st, grid, shared_tiles, routed_tiles);
   } else {
-    if (sp.r == 2) gu_nt<W_MXFP4, 1, 2>(a, st, grid, shared_tiles, routed_tiles);
+    if (sp.r == 1) gu_nt<W_MXFP4, 1, 1>(a, st, grid, shared_tiles, routed_tiles);
+    else if (sp.r == 2) gu_nt<W_MXFP4, 1, 2>(a, st, grid, shared_tiles, routed_tiles);
     else gu_nt<W_MXFP4, 1, 4>(a, st, grid, shared_tiles, routed_tiles);
   }
   return hipGetLastError();
@@ -580,6 +584,7 @@ hipError_t launch_ffn_down(int wtype, const FfnArgs& a, hipStream_t st) {
   const unsigned grid = shared_tiles + a.routed_items * tiles;
   if (!grid) return hipSuccess;
   if (wtype == W_BF16) dn_nt<W_BF16, 1, 2>(a, st, grid, shared_tiles, tiles);
+  else if (sp.r == 1) dn_nt<W_MXFP4, 1, 1>(a, st, grid, shared_tiles, tiles);
   else if (sp.r == 2) dn_nt<W_MXFP4, 1, 2>(a, st, grid, shared_tiles, tiles);
   else dn_nt<W_MXFP4, 1, 4>(a, st, grid, shared_tiles, tiles);
   return hipGetLastError();

@@ -4,7 +4,7 @@
 // on a Single Workstation GPU" (MarkTechPost).  Routing is left exactly as the
 // router decides ("Three mechanisms": bandwidth-adaptive execution, no router
 // modification; "Key Takeaways": bit-exact expert output) and the experts'
-// partial sums merge exactly ("Three mechanisms").
+// partial sums are added without approximation ("Three mechanisms").
 #include <climits>
 
 #include "common.hpp"

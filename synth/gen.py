@@ -11,7 +11,7 @@ Formats
   shared exponent is floor(log2(amax)) - 2 (2 is the largest E2M1 exponent) and
   each element is rounded to nearest-even E2M1, saturating at +-6.
 
-Expert slot layout ("final host layout": one expert is one contiguous run of
+Expert slot layout (the layout experts are kept in, host and device: one expert is one contiguous run of
 ``expert_bytes`` so a cache fill is a single copy)::
 
     f32   :  W13 [2I][H] then W2 [H][I], row-major, rows K-contiguous;
