@@ -77,10 +77,16 @@ def progress(msg):
 
 
 def ffn_source_hash():
+    """Hash of the FFN kernel sources with comments and whitespace removed (a
+    comment edit does not change the kernels the counters describe)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in FFN_SOURCES:
-        h.update(open(f, "rb").read())
+        src = open(f).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 
