@@ -39,6 +39,10 @@ template <typename K, typename... Args>
 static void launch_ffn_kernel(K kernel, unsigned grid, hipStream_t st, Args... args) {
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, args...);
 }
+template <typename K, typename... Args>
+static void launch_ffn_kernel_lds(K kernel, unsigned grid, size_t lds, hipStream_t st, Args... args) {
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, st, args...);
+}
 
 // ===========================================================================
 // f32 weights: plain FMA, one wave per output element row, lanes split K,
@@ -152,7 +156,7 @@ struct Chunk {
 // re-read step s1-1 (never computed) and MXFP4 column groups past K (zero codes
 // in the padded tile) re-read the row's last 8 values, so every access stays in
 // its buffer.
-template <int WT, int NT, int R, int U, bool CLAMP, bool SCALES = true>
+template <int WT, int NT, int R, int U, bool CLAMP, bool SCALES = true, bool LB = false>
 __device__ __forceinline__ void load_chunk(Chunk<WT, NT, R, U>& c, const Mat& w, const int (&atile)[R], int s,
                                            int s1, int g, const Rows& rows, const int (&brow)[NT], int ntl) {
   constexpr int KS = KStep<WT>::value;
@@ -171,6 +175,7 @@ __device__ __forceinline__ void load_chunk(Chunk<WT, NT, R, U>& c, const Mat& w,
         c.qs[u][t] = 0u;
     }
   }
+  if constexpr (LB) return;  // token fragments come from LDS at compute time
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     if (nt < ntl) {
@@ -195,11 +200,24 @@ __device__ __forceinline__ void load_chunk(Chunk<WT, NT, R, U>& c, const Mat& w,
 
 // MFMAs of one chunk.  MXFP4 scales come from the chunk's per-step words, or,
 // with a scale block `sb` (16 steps per row tile, this lane's 16 bytes), from
-// byte sofs + u of it (sofs = the chunk's first step inside the block).
-template <int WT, int NT, int R, int U, bool BLOCK = false>
+// byte sofs + u of it (sofs = the chunk's first step inside the block).  Token
+// fragments come from the chunk's registers, or with LB from the pass's rows in
+// LDS (row brow[nt], the same column clamp as the global loads).
+template <int WT, int NT, int R, int U, bool BLOCK = false, bool LB = false>
 __device__ __forceinline__ void compute_chunk(const Chunk<WT, NT, R, U>& c, int s, int s1, int ntl,
-                                              f32x4 (&acc)[R][NT], const u32x4* sb = nullptr, int sofs = 0) {
+                                              f32x4 (&acc)[R][NT], const u32x4* sb, int sofs, const Rows& rows,
+                                              const int (&brow)[NT], int K) {
   constexpr int NA = Chunk<WT, NT, R, U>::NA;
+  constexpr int KS = KStep<WT>::value;
+  auto bfrag = [&](int u, int nt, int m) -> bf16x8 {
+    if constexpr (LB) {
+      const int g = (threadIdx.x & 63) >> 4;
+      const int kk = WT == W_MXFP4 ? min((s + u) * KS + 32 * g + 8 * m, K - 8) : (s + u) * KS + 8 * g;
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(rows.lds + brow[nt] * rows.lds_ld + kk * 2));
+    } else {
+      return as_bf16x8(c.qb[u][nt][m]);
+    }
+  };
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (BLOCK || s + u < s1) {
@@ -219,8 +237,7 @@ __device__ __forceinline__ void compute_chunk(const Chunk<WT, NT, R, U>& c, int 
           if (nt < ntl) {
 #pragma unroll
             for (int m = 0; m < NA; ++m)
-              acc[t][nt] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m], as_bf16x8(c.qb[u][nt][m]), acc[t][nt], 0, 0, 0);
+              acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m], bfrag(u, nt, m), acc[t][nt], 0, 0, 0);
           }
         }
       }
@@ -234,7 +251,7 @@ __device__ __forceinline__ void compute_chunk(const Chunk<WT, NT, R, U>& c, int 
 // chunk c is computed, so a wave keeps between U and 2U steps of weight loads
 // outstanding; each token fragment is loaded once per step and reused by the R
 // weight tiles.
-template <int WT, int NT, int R>
+template <int WT, int NT, int R, bool LB = false>
 __device__ __forceinline__ void mfma_rows(const Mat& w, const int (&atile)[R], int s0, int s1, int g,
                                           const Rows& rows, const int (&brow)[NT], int ntl, f32x4 (&acc)[R][NT]) {
   constexpr int U = Unroll<WT, NT, R>::value;
@@ -260,14 +277,15 @@ __device__ __forceinline__ void mfma_rows(const Mat& w, const int (&atile)[R], i
 #pragma unroll
         for (int i = 0; i < 16 / (2 * U); ++i) {
           const int s = sblk + 2 * U * i;
-          load_chunk<WT, NT, R, U, false, false>(c1, w, atile, s + U, s1, g, rows, brow, ntl);
-          compute_chunk<WT, NT, R, U, true>(c0, s, s1, ntl, acc, cur, 2 * U * i);
-          load_chunk<WT, NT, R, U, false, false>(c0, w, atile, min(s + 2 * U, s1 - U), s1, g, rows, brow, ntl);
-          compute_chunk<WT, NT, R, U, true>(c1, s + U, s1, ntl, acc, cur, 2 * U * i + U);
+          load_chunk<WT, NT, R, U, false, false, LB>(c1, w, atile, s + U, s1, g, rows, brow, ntl);
+          compute_chunk<WT, NT, R, U, true, LB>(c0, s, s1, ntl, acc, cur, 2 * U * i, rows, brow, w.K);
+          load_chunk<WT, NT, R, U, false, false, LB>(c0, w, atile, min(s + 2 * U, s1 - U), s1, g, rows, brow,
+                                                     ntl);
+          compute_chunk<WT, NT, R, U, true, LB>(c1, s + U, s1, ntl, acc, cur, 2 * U * i + U, rows, brow, w.K);
         }
       };
       load_sb(sb[0], s0);
-      load_chunk<WT, NT, R, U, false, false>(c0, w, atile, s0, s1, g, rows, brow, ntl);
+      load_chunk<WT, NT, R, U, false, false, LB>(c0, w, atile, s0, s1, g, rows, brow, ntl);
       for (int b = 0; b < nb; b += 2) {
         block(sb[0], sb[1], s0 + 16 * b);
         if (b + 1 < nb) block(sb[1], sb[0], s0 + 16 * (b + 1));
@@ -276,21 +294,22 @@ __device__ __forceinline__ void mfma_rows(const Mat& w, const int (&atile)[R], i
     }
   }
   if ((s1 - s0) % (2 * U) == 0 && (WT != W_MXFP4 || w.K % 128 == 0)) {
-    load_chunk<WT, NT, R, U, false>(c0, w, atile, s0, s1, g, rows, brow, ntl);
+    load_chunk<WT, NT, R, U, false, true, LB>(c0, w, atile, s0, s1, g, rows, brow, ntl);
     for (int s = s0; s < s1; s += 2 * U) {
-      load_chunk<WT, NT, R, U, false>(c1, w, atile, s + U, s1, g, rows, brow, ntl);
-      compute_chunk<WT, NT, R, U>(c0, s, s1, ntl, acc);
-      if (s + 2 * U < s1) load_chunk<WT, NT, R, U, false>(c0, w, atile, s + 2 * U, s1, g, rows, brow, ntl);
-      compute_chunk<WT, NT, R, U>(c1, s + U, s1, ntl, acc);
+      load_chunk<WT, NT, R, U, false, true, LB>(c1, w, atile, s + U, s1, g, rows, brow, ntl);
+      compute_chunk<WT, NT, R, U, false, LB>(c0, s, s1, ntl, acc, nullptr, 0, rows, brow, w.K);
+      if (s + 2 * U < s1)
+        load_chunk<WT, NT, R, U, false, true, LB>(c0, w, atile, s + 2 * U, s1, g, rows, brow, ntl);
+      compute_chunk<WT, NT, R, U, false, LB>(c1, s + U, s1, ntl, acc, nullptr, 0, rows, brow, w.K);
     }
     return;
   }
-  load_chunk<WT, NT, R, U, true>(c0, w, atile, s0, s1, g, rows, brow, ntl);
+  load_chunk<WT, NT, R, U, true, true, LB>(c0, w, atile, s0, s1, g, rows, brow, ntl);
   for (int s = s0; s < s1; s += 2 * U) {
-    load_chunk<WT, NT, R, U, true>(c1, w, atile, s + U, s1, g, rows, brow, ntl);
-    compute_chunk<WT, NT, R, U>(c0, s, s1, ntl, acc);
-    load_chunk<WT, NT, R, U, true>(c0, w, atile, s + 2 * U, s1, g, rows, brow, ntl);
-    compute_chunk<WT, NT, R, U>(c1, s + U, s1, ntl, acc);
+    load_chunk<WT, NT, R, U, true, true, LB>(c1, w, atile, s + U, s1, g, rows, brow, ntl);
+    compute_chunk<WT, NT, R, U, false, LB>(c0, s, s1, ntl, acc, nullptr, 0, rows, brow, w.K);
+    load_chunk<WT, NT, R, U, true, true, LB>(c0, w, atile, s + 2 * U, s1, g, rows, brow, ntl);
+    compute_chunk<WT, NT, R, U, false, LB>(c1, s + U, s1, ntl, acc, nullptr, 0, rows, brow, w.K);
   }
 }
 
@@ -299,10 +318,25 @@ __device__ __forceinline__ void mfma_rows(const Mat& w, const int (&atile)[R], i
 // in a fixed order through LDS.  A block therefore covers 16 * R * (4/KW) rows of
 // one item.
 
+// Token rows of a pass in LDS (LB kernels): the block copies the pass's np real
+// rows, K bf16 each, into rows of K*2 + 16 bytes (the 16 bytes of padding put the
+// 16 rows of one 128-bit read on different banks); row_start(i) is the element
+// offset of pass row i in `src`.  Lane rows past np re-read row np-1.
+template <typename RowStart>
+__device__ __forceinline__ void stage_rows(uint8_t* lds, const uint16_t* src, int np, int K,
+                                           const RowStart& row_start) {
+  const int pieces = K / 8, ld = K * 2 + 16;
+  for (int q = threadIdx.x; q < np * pieces; q += blockDim.x) {
+    const int row = q / pieces, pc = q - row * pieces;
+    *reinterpret_cast<u32x4*>(lds + row * ld + pc * 16) =
+        *reinterpret_cast<const u32x4*>(src + row_start(row) + (size_t)pc * 8);
+  }
+}
+
 // gate_up: row tile t of a wave is 8 intermediate indices j..j+7 of one item: one
 // 16-row A tile = gate rows j..j+7 stacked on up rows j..j+7, so the epilogue
 // pairs lane l (gate) with lane l+32 (up) and writes h = SiLU(gate) * up as bf16.
-template <int WT, int NT, int KW, int R>
+template <int WT, int NT, int KW, int R, bool LB = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT, NT>::waves))) void gate_up_mfma(
     FfnArgs a, int shared_tiles, int routed_tiles) {
   constexpr int RT = 4 / KW;
@@ -326,6 +360,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
   Rows rows;
   rows.buf = make_rsrc(a.x, (size_t)a.T * H * 2);
   rows.ld = H;
+  rows.lds = nullptr;
+  rows.lds_ld = 0;
   uint16_t* h = reinterpret_cast<uint16_t*>(a.h);
   for (int pass = 0; pass < it.n; pass += NT * 16) {
     const int ntl = min(NT, (it.n - pass + 15) / 16);
@@ -335,13 +371,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
       const int i = min(pass + nt * 16 + r, it.n - 1);  // padding columns re-read a real row
       xrow[nt] = item_token(a, it, i);
     }
+    if constexpr (LB) {
+      extern __shared__ __attribute__((aligned(16))) uint8_t lds_rows[];
+      const int np = min(NT * 16, it.n - pass);
+      if (pass > 0) __syncthreads();  // the previous pass has finished reading
+      stage_rows(lds_rows, reinterpret_cast<const uint16_t*>(a.x), np, H,
+                 [&](int i) { return (size_t)item_token(a, it, pass + i) * H; });
+      __syncthreads();
+      rows.lds = lds_rows;
+      rows.lds_ld = H * 2 + 16;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) xrow[nt] = min(nt * 16 + r, np - 1);
+    }
     f32x4 acc[R][NT];
 #pragma unroll
     for (int t = 0; t < R; ++t)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (ntiles == R) {
-      mfma_rows<WT, NT, R>(w, atile, s0, s1, g, rows, xrow, ntl, acc);
+      mfma_rows<WT, NT, R, LB>(w, atile, s0, s1, g, rows, xrow, ntl, acc);
     } else if (ntiles > 0) {
       // ragged last tiles of the item: one tile at a time
       for (int t = 0; t < ntiles; ++t) {
@@ -349,7 +397,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) one[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int tile1[1] = {j0 / 8 + t};
-        mfma_rows<WT, NT, 1>(w, tile1, s0, s1, g, rows, xrow, ntl, one);
+        mfma_rows<WT, NT, 1, LB>(w, tile1, s0, s1, g, rows, xrow, ntl, one);
 #pragma unroll
         for (int tt = 0; tt < R; ++tt)
           if (tt == t)
@@ -398,7 +446,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
 }
 
 // down: row tile t of a wave is 16 output columns (rows of W2) of one item.
-template <int WT, int NT, int KW, int R>
+template <int WT, int NT, int KW, int R, bool LB = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT, NT>::waves))) void down_mfma(
     FfnArgs a, int shared_tiles, int routed_tiles) {
   constexpr int RT = 4 / KW;
@@ -417,6 +465,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
   Rows rows;
   rows.buf = make_rsrc(a.h, ((size_t)a.T * a.k + (a.shared_w ? a.T : 0)) * a.h_ld * 2);
   rows.ld = a.h_ld;
+  rows.lds = nullptr;
+  rows.lds_ld = 0;
   for (int pass = 0; pass < it.n; pass += NT * 16) {
     const int ntl = min(NT, (it.n - pass + 15) / 16);
     int hrow[NT];
@@ -424,6 +474,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
     for (int nt = 0; nt < NT; ++nt) {
       const int i = min(pass + nt * 16 + r, it.n - 1);  // padding columns re-read a real row
       hrow[nt] = it.hrow0 + i;
+    }
+    if constexpr (LB) {
+      extern __shared__ __attribute__((aligned(16))) uint8_t lds_rows[];
+      const int np = min(NT * 16, it.n - pass);
+      if (pass > 0) __syncthreads();  // the previous pass has finished reading
+      stage_rows(lds_rows, reinterpret_cast<const uint16_t*>(a.h), np, Ie,
+                 [&](int i) { return (size_t)(it.hrow0 + pass + i) * a.h_ld; });
+      __syncthreads();
+      rows.lds = lds_rows;
+      rows.lds_ld = Ie * 2 + 16;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) hrow[nt] = min(nt * 16 + r, np - 1);
     }
     f32x4 acc[R][NT];
 #pragma unroll
@@ -434,14 +496,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
       int atile[R];
 #pragma unroll
       for (int t = 0; t < R; ++t) atile[t] = row0 / 16 + t;
-      mfma_rows<WT, NT, R>(w, atile, s0, s1, g, rows, hrow, ntl, acc);
+      mfma_rows<WT, NT, R, LB>(w, atile, s0, s1, g, rows, hrow, ntl, acc);
     } else if (ntiles > 0) {
       for (int t = 0; t < ntiles; ++t) {
         f32x4 one[1][NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) one[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int tile1[1] = {row0 / 16 + t};
-        mfma_rows<WT, NT, 1>(w, tile1, s0, s1, g, rows, hrow, ntl, one);
+        mfma_rows<WT, NT, 1, LB>(w, tile1, s0, s1, g, rows, hrow, ntl, one);
 #pragma unroll
         for (int tt = 0; tt < R; ++tt)
           if (tt == t)
@@ -523,10 +585,30 @@ static int pick_nt(int T, int wtype) {
   return wtype == W_MXFP4 && nt > MOE_DEC_MX_NTMAX ? MOE_DEC_MX_NTMAX : nt;
 }
 
+// MXFP4 passes of one token tile take their token rows from LDS (staged once per
+// pass and block) when the batch has at least MOE_DEC_LDS_MIN_T tokens (below, the
+// staging costs more than it saves) and min(T, 16) rows of K columns fit in
+// MOE_DEC_LDS_ROWS_MAX bytes (above, LDS would cap the blocks per CU).
+#ifndef MOE_DEC_LDS_ROWS_MAX
+#define MOE_DEC_LDS_ROWS_MAX 65536
+#endif
+#ifndef MOE_DEC_LDS_MIN_T
+#define MOE_DEC_LDS_MIN_T 4
+#endif
+static size_t lds_rows_bytes(int T, int K) {
+  return T < MOE_DEC_LDS_MIN_T ? (size_t)-1 : (size_t)(T < 16 ? T : 16) * ((size_t)K * 2 + 16);
+}
+
 template <int WT, int KW, int R>
 static void gu_nt(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int rt) {
+  const size_t lb = lds_rows_bytes(a.T, a.H);
   switch (pick_nt(a.T, WT)) {
-    case 1: launch_ffn_kernel(gate_up_mfma<WT, 1, KW, R>, grid, st, a, sh, rt); break;
+    case 1:
+      if (WT == W_MXFP4 && KW == 1 && lb <= MOE_DEC_LDS_ROWS_MAX)
+        launch_ffn_kernel_lds(gate_up_mfma<WT, 1, KW, R, WT == W_MXFP4 && KW == 1>, grid, lb, st, a, sh, rt);
+      else
+        launch_ffn_kernel(gate_up_mfma<WT, 1, KW, R>, grid, st, a, sh, rt);
+      break;
     case 2: launch_ffn_kernel(gate_up_mfma<WT, 2, KW, R>, grid, st, a, sh, rt); break;
     case 4: launch_ffn_kernel(gate_up_mfma<WT, 4, KW, R>, grid, st, a, sh, rt); break;
     default: launch_ffn_kernel(gate_up_mfma<WT, 8, KW, R>, grid, st, a, sh, rt); break;
@@ -534,8 +616,14 @@ static void gu_nt(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int r
 }
 template <int WT, int KW, int R>
 static void dn_nt(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int rt) {
+  const size_t lb = lds_rows_bytes(a.T, a.I > a.I_shared ? a.I : a.I_shared);
   switch (pick_nt(a.T, WT)) {
-    case 1: launch_ffn_kernel(down_mfma<WT, 1, KW, R>, grid, st, a, sh, rt); break;
+    case 1:
+      if (WT == W_MXFP4 && KW == 1 && lb <= MOE_DEC_LDS_ROWS_MAX)
+        launch_ffn_kernel_lds(down_mfma<WT, 1, KW, R, WT == W_MXFP4 && KW == 1>, grid, lb, st, a, sh, rt);
+      else
+        launch_ffn_kernel(down_mfma<WT, 1, KW, R>, grid, st, a, sh, rt);
+      break;
     case 2: launch_ffn_kernel(down_mfma<WT, 2, KW, R>, grid, st, a, sh, rt); break;
     case 4: launch_ffn_kernel(down_mfma<WT, 4, KW, R>, grid, st, a, sh, rt); break;
     default: launch_ffn_kernel(down_mfma<WT, 8, KW, R>, grid, st, a, sh, rt); break;

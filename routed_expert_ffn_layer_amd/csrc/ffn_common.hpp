@@ -73,11 +73,13 @@ struct Mat {
   int K;                          // columns
 };
 
-// Token rows of the B operand: a buffer, the row stride in elements, and per
-// token column nt this lane's row index.
+// Token rows of the B operand: a buffer and its row stride in elements; when the
+// pass's rows are staged in LDS, row i of the pass sits at lds + i * lds_ld.
 struct Rows {
   __amdgpu_buffer_rsrc_t buf;
   int ld;
+  const uint8_t* lds;
+  int lds_ld;
 };
 
 constexpr int kBufferFlags = 0x00020000;  // raw (untyped) 32-bit buffer access

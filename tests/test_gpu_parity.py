@@ -130,6 +130,8 @@ SMALL = [
     (synth.MXFP4, 24, 2048, 2048, 4, 2, False),
     (synth.MXFP4, 6, 2048, 2048, 3, 2, True),
     (synth.MXFP4, 40, 2048, 2048, 2, 2, False),
+    # token rows staged in LDS with K not a multiple of 128 (clamped columns), shared expert
+    (synth.MXFP4, 5, 160, 96, 8, 2, True),
 ]
 
 
