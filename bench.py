@@ -63,6 +63,8 @@ def parse():
                     help="distinct layers kept in pinned host memory (layer l reads host layer l mod this)")
     ap.add_argument("--distinct-experts", type=int, default=512,
                     help="decode_mxfp4: distinct generated experts copied into the 11,008 slots")
+    ap.add_argument("--split-waves", action="store_true",
+                    help="cached_trace_bf16: compute each wave's hits while its misses fill (default: after all fills)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -725,11 +727,13 @@ def workload_cached_trace_bf16(args):
                            .view(np.int16)).to(dev) for l in range(n_layers)]
     b = L.LayerBuffers(1, E, k, H, I, moe.MOE_BF16)
 
+    fwd = L.forward_cached_split if args.split_waves else L.forward_cached
+
     def run(cache, n_tok):
         tot = dict(accesses=0, hits=0, misses=0, fill_bytes=0, waves=0)
         for t in range(n_tok):
             for l in range(n_layers):
-                _, waves = L.forward_cached(b, cache, l, trace_d[t, l:l + 1], xs[l], slot_pool, stride)
+                _, waves = fwd(b, cache, l, trace_d[t, l:l + 1], xs[l], slot_pool, stride)
                 for key in ("accesses", "hits", "misses"):  # per step, repeated by every wave's call
                     tot[key] += waves[0][key]
                 tot["fill_bytes"] += sum(w["fill_bytes"] for w in waves)
@@ -760,7 +764,8 @@ def workload_cached_trace_bf16(args):
         {"workload": "cached decode trace bf16: 1000 tokens x 48 layers, hidden 2048, 256 experts, top-8, "
                      "intermediate 512, global LRU over 37% of the experts", "tokens": tokens,
          "stacked_layers": n_layers, "slots": S, "slot_pool_gb": round(S * stride / 1e9, 2),
-         "host_layers_distinct": n_host},
+         "host_layers_distinct": n_host,
+         "waves": "split (hits computed while misses fill)" if args.split_waves else "whole (FFN after all fills)"},
         {"kernel": "expert fills (hipMemcpyAsync pinned host -> HBM slots)", "bound": "pcie",
          "achieved": fill_gbs, "peak": bp, "unit": "GB/s", "frac": fill_gbs / bp, "traffic": None,
          "timing": "wall clock of the whole trace; peak = measured pinned host -> HBM bandwidth at one expert"},

@@ -8,6 +8,7 @@
  *   moe_route_topk         top-k gating over router logits
  *   moe_permute            stable permutation of (token, choice) pairs by expert
  *   moe_cache_lookup_fill  global-LRU expert-slot cache in HBM, filled from pinned host memory
+ *                          (moe_cache_lookup_fill_split + moe_cache_wait_fills: hits computed during fills)
  *   moe_grouped_ffn        grouped SwiGLU expert FFN (f32, bf16 or MXFP4 weights)
  *   moe_combine            gate-weighted merge of the expert outputs
  *   moe_layer_stream_*     whole-layer double buffering for prefill
@@ -17,7 +18,7 @@
  *  - Every call returns a moe_status; nothing throws, aborts or exits.  On failure
  *    moe_last_error() holds a message for the calling thread.
  *  - Calls that take a hipStream_t are asynchronous on it, except
- *    moe_cache_lookup_fill for wave 0 (it waits for the step's expert counts).
+ *    moe_cache_lookup_fill(_split) for wave 0 (it waits for the step's expert counts).
  *  - The caller owns every buffer and stream.  The library owns only the opaque
  *    handles (host metadata and HIP events) and allocates no device memory on the
  *    hot path: scratch comes from the caller through moe_grouped_ffn_workspace().
@@ -105,6 +106,12 @@ int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, 
 int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
                 int32_t* sorted_rows, int32_t* inv_rows, hipStream_t stream);
 
+/* moe_route_topk followed by moe_permute on the same buffers, with the same
+ * arguments, requirements and results; batches of at most 64 tokens run as one
+ * workgroup launch (one launch fewer per decode layer). */
+int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w, int32_t* counts,
+              int32_t* offsets, int32_t* sorted_rows, int32_t* inv_rows, hipStream_t stream);
+
 /* ------------------------------------------------------------------------- */
 /* Expert-slot cache.  The pages: inactive experts sit in host memory and enter
  * the execution path on demand ("The gap it targets"); during decode a shared
@@ -167,6 +174,25 @@ int moe_cache_destroy(moe_cache* c);
  * overwritten; the rest of the state is as before the call. */
 int moe_cache_lookup_fill(moe_cache* c, int layer, const int32_t* counts, int wave,
                           int32_t* slot_of_expert, moe_cache_stats* stats_host, hipStream_t compute_stream);
+
+/* Split lookup, for computing the resident experts while the misses stream in
+ * (the pages: the GPU keeps computing what it holds while missing experts are
+ * transferred, "Three mechanisms", bandwidth-adaptive execution).  Same plan,
+ * fills, ordering of waves and errors as moe_cache_lookup_fill, but two device
+ * tables [n_experts] are written on compute_stream: slot_hits holds the slots of
+ * the wave's hits (-1 elsewhere) and may be used at once, since hits are never
+ * victims of the wave's misses; slot_misses holds the slots of the wave's filled
+ * experts (-1 elsewhere) and may be used only after moe_cache_wait_fills.  The
+ * caller runs the FFN over slot_hits, then moe_cache_wait_fills, then the FFN over
+ * slot_misses (skipped when stats->fill_bytes is 0); the two FFNs write disjoint
+ * output rows, so the layer equals the unsplit one bit for bit.  Both pointers
+ * must be 16-byte aligned and distinct. */
+int moe_cache_lookup_fill_split(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_hits,
+                                int32_t* slot_misses, moe_cache_stats* stats_host, hipStream_t compute_stream);
+/* Makes compute_stream wait for the fills of the last split lookup (no-op if it
+ * had none or they were already waited for).  A later lookup on the handle
+ * inserts this wait itself if the caller skipped it. */
+int moe_cache_wait_fills(moe_cache* c, hipStream_t compute_stream);
 
 /* Same policy without any device work: counts_host in, slot table and the list
  * of fills (slot, layer, expert, wave) out, for the caller to perform.  Works on

@@ -124,6 +124,22 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, i
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_permute launch");
 }
 
+int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w, int32_t* counts,
+              int32_t* offsets, int32_t* sorted_rows, int32_t* inv_rows, hipStream_t stream) {
+  if (int rc = check_routing(T, E, k)) return rc;
+  REQUIRE_PTR(counts);
+  REQUIRE_PTR(offsets);
+  if (T > 0) {
+    REQUIRE_PTR(logits);
+    REQUIRE_PTR(topk_ids);
+    REQUIRE_PTR(topk_w);
+    REQUIRE_PTR(sorted_rows);
+    REQUIRE_PTR(inv_rows);
+  }
+  hipError_t e = moe::launch_route(logits, T, E, k, topk_ids, topk_w, counts, offsets, sorted_rows, inv_rows, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route launch");
+}
+
 int moe_combine(const float* out_rows, const float* topk_w, const int32_t* inv_rows, const float* shared_out, int T,
                 int k, int H, void* y, int ydt, hipStream_t stream) {
   if (T < 0 || k < 1 || k > 32 || H <= 0 || H % 4) return fail(MOE_EINVAL, "moe_combine: bad T=%d k=%d H=%d", T, k, H);
@@ -245,11 +261,12 @@ struct moe_cache {
   moe_cache_desc desc;
   bool device = false;
   int32_t* counts_pinned = nullptr;       // [E]
-  int32_t* stage_pinned = nullptr;        // [kStages][E]
+  int32_t* stage_pinned = nullptr;        // [kStages][2E] (a split lookup uploads two tables)
   hipEvent_t stage_ev[8] = {};
   bool stage_used[8] = {};
   int stage_next = 0;
   hipEvent_t ev_counts = nullptr, ev_compute = nullptr, ev_fill = nullptr;
+  bool fill_pending = false;              // a split lookup's fills not yet waited for
   int64_t fail_after = -1;                // injected failure: fills left before one fails
   std::vector<moe::PlannedFill> fills;
   std::vector<int32_t> table;
@@ -333,7 +350,7 @@ int moe_cache_create(const moe_cache_desc* d, moe_cache** out) {
   if (device) {
     hipError_t e = hipHostMalloc((void**)&c->counts_pinned, sizeof(int32_t) * d->n_experts, hipHostMallocDefault);
     if (e == hipSuccess)
-      e = hipHostMalloc((void**)&c->stage_pinned, sizeof(int32_t) * d->n_experts * kStages, hipHostMallocDefault);
+      e = hipHostMalloc((void**)&c->stage_pinned, sizeof(int32_t) * 2 * d->n_experts * kStages, hipHostMallocDefault);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_counts, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fill, hipEventDisableTiming);
@@ -411,20 +428,39 @@ int moe_cache_lookup_host(moe_cache* c, int layer, const int32_t* counts_host, i
   return MOE_OK;
 }
 
-int moe_cache_lookup_fill(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_of_expert,
-                          moe_cache_stats* stats_host, hipStream_t compute_stream) {
+}  // extern "C"
+
+namespace {
+
+// Lookup of one wave on the device cache.  Without `slot_misses` the wave's
+// fills are awaited on the compute stream and `slot_a` is the whole table; with
+// it, `slot_a` holds the hits only (usable at once: hits are never victims of
+// the wave's misses) and `slot_misses` the filled experts only, and the compute
+// stream waits for the fills only at moe_cache_wait_fills.
+int lookup_fill_device(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_a,
+                       int32_t* slot_misses, moe_cache_stats* stats_host, hipStream_t compute_stream,
+                       const char* what) {
   if (!c) return fail(MOE_EINVAL, "null cache");
-  if (!c->device) return fail(MOE_EINVAL, "moe_cache_lookup_fill needs a device cache (slot_pool set)");
-  REQUIRE_PTR(slot_of_expert);
+  if (!c->device) return fail(MOE_EINVAL, "%s needs a device cache (slot_pool set)", what);
+  if (!slot_a || !aligned16(slot_a)) return fail(MOE_EINVAL, "%s: slot table must be a 16-byte aligned pointer", what);
+  if (slot_misses && !aligned16(slot_misses))
+    return fail(MOE_EINVAL, "%s: slot_misses must be a 16-byte aligned pointer", what);
+  const bool split = slot_misses != nullptr;
   const int E = c->desc.n_experts;
   hipError_t e;
+  if (c->fill_pending) {
+    // a split wave whose fills were never awaited: order them before anything else
+    e = hipStreamWaitEvent(compute_stream, c->ev_fill, 0);
+    if (e != hipSuccess) return hip_fail(e, (std::string(what) + ": fencing earlier fills").c_str());
+    c->fill_pending = false;
+  }
   if (wave == 0) {
-    REQUIRE_PTR(counts);
+    if (!counts) return fail(MOE_EINVAL, "%s: null counts", what);
     // The one host synchronisation of the layer: the step's counts.
     e = hipMemcpyAsync(c->counts_pinned, counts, sizeof(int32_t) * E, hipMemcpyDeviceToHost, compute_stream);
     if (e == hipSuccess) e = hipEventRecord(c->ev_counts, compute_stream);
     if (e == hipSuccess) e = hipEventSynchronize(c->ev_counts);
-    if (e != hipSuccess) return hip_fail(e, "moe_cache_lookup_fill: reading counts");
+    if (e != hipSuccess) return hip_fail(e, (std::string(what) + ": reading counts").c_str());
   }
   int nacc = 0;
   if (int rc = plan(c, layer, c->counts_pinned, wave, &nacc)) return rc;
@@ -435,46 +471,84 @@ int moe_cache_lookup_fill(moe_cache* c, int layer, const int32_t* counts, int wa
     if (e == hipSuccess) e = hipStreamWaitEvent(c->desc.fill_stream, c->ev_compute, 0);
     if (e != hipSuccess) {
       c->core.abort_step();
-      return hip_fail(e, "moe_cache_lookup_fill: fencing fills");
+      return hip_fail(e, (std::string(what) + ": fencing fills").c_str());
     }
     for (size_t i = 0; i < c->fills.size(); ++i) {
       const moe::PlannedFill& f = c->fills[i];
       if (injected_failure(c)) {
         invalidate_upto(c, i + 1);
-        return fail(MOE_EHIP, "moe_cache_lookup_fill: injected fill failure at fill %zu", i);
+        return fail(MOE_EHIP, "%s: injected fill failure at fill %zu", what, i);
       }
       void* dst = static_cast<uint8_t*>(c->desc.slot_pool) + (size_t)f.slot * c->desc.slot_stride;
       e = hipMemcpyAsync(dst, host_src(c, layer, f.expert), c->desc.expert_bytes, hipMemcpyHostToDevice,
                          c->desc.fill_stream);
       if (e != hipSuccess) {
         invalidate_upto(c, i + 1);
-        return hip_fail(e, "moe_cache_lookup_fill: fill copy");
+        return hip_fail(e, (std::string(what) + ": fill copy").c_str());
       }
       bytes += (int64_t)c->desc.expert_bytes;
     }
-    // read-after-write: the FFN of this wave waits for its fills
+    // read-after-write: the FFN over the filled experts waits for the fills
     e = hipEventRecord(c->ev_fill, c->desc.fill_stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(compute_stream, c->ev_fill, 0);
+    if (e == hipSuccess && !split) e = hipStreamWaitEvent(compute_stream, c->ev_fill, 0);
     if (e != hipSuccess) {
       invalidate_upto(c, c->fills.size());
-      return hip_fail(e, "moe_cache_lookup_fill: fencing compute");
+      return hip_fail(e, (std::string(what) + ": fencing compute").c_str());
     }
+    c->fill_pending = split;
   }
   c->core.commit_wave(wave);
-  // slot table upload through a ring of pinned staging buffers
+  // slot table(s) upload through a ring of pinned staging buffers
   const int q = c->stage_next;
   c->stage_next = (q + 1) % kStages;
   if (c->stage_used[q]) {
     e = hipEventSynchronize(c->stage_ev[q]);
-    if (e != hipSuccess) return hip_fail(e, "moe_cache_lookup_fill: staging buffer");
+    if (e != hipSuccess) return hip_fail(e, (std::string(what) + ": staging buffer").c_str());
   }
-  int32_t* stage = c->stage_pinned + (size_t)q * E;
+  int32_t* stage = c->stage_pinned + (size_t)q * 2 * E;
   for (int x = 0; x < E; ++x) stage[x] = c->table[x];
-  e = hipMemcpyAsync(slot_of_expert, stage, sizeof(int32_t) * E, hipMemcpyHostToDevice, compute_stream);
+  if (split) {
+    int32_t* miss = stage + E;
+    for (int x = 0; x < E; ++x) miss[x] = -1;
+    for (const moe::PlannedFill& f : c->fills) {
+      miss[f.expert] = stage[f.expert];
+      stage[f.expert] = -1;
+    }
+  }
+  e = hipMemcpyAsync(slot_a, stage, sizeof(int32_t) * E, hipMemcpyHostToDevice, compute_stream);
+  if (e == hipSuccess && split)
+    e = hipMemcpyAsync(slot_misses, stage + E, sizeof(int32_t) * E, hipMemcpyHostToDevice, compute_stream);
   if (e == hipSuccess) e = hipEventRecord(c->stage_ev[q], compute_stream);
-  if (e != hipSuccess) return hip_fail(e, "moe_cache_lookup_fill: slot table upload");
+  if (e != hipSuccess) return hip_fail(e, (std::string(what) + ": slot table upload").c_str());
   c->stage_used[q] = true;
   fill_stats(c, nacc, bytes, stats_host);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_cache_lookup_fill(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_of_expert,
+                          moe_cache_stats* stats_host, hipStream_t compute_stream) {
+  return lookup_fill_device(c, layer, counts, wave, slot_of_expert, nullptr, stats_host, compute_stream,
+                            "moe_cache_lookup_fill");
+}
+
+int moe_cache_lookup_fill_split(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_hits,
+                                int32_t* slot_misses, moe_cache_stats* stats_host, hipStream_t compute_stream) {
+  if (!slot_misses) return fail(MOE_EINVAL, "moe_cache_lookup_fill_split: null slot_misses");
+  return lookup_fill_device(c, layer, counts, wave, slot_hits, slot_misses, stats_host, compute_stream,
+                            "moe_cache_lookup_fill_split");
+}
+
+int moe_cache_wait_fills(moe_cache* c, hipStream_t compute_stream) {
+  if (!c) return fail(MOE_EINVAL, "null cache");
+  if (!c->device) return fail(MOE_EINVAL, "moe_cache_wait_fills needs a device cache (slot_pool set)");
+  if (!c->fill_pending) return MOE_OK;
+  const hipError_t e = hipStreamWaitEvent(compute_stream, c->ev_fill, 0);
+  if (e != hipSuccess) return hip_fail(e, "moe_cache_wait_fills");
+  c->fill_pending = false;
   return MOE_OK;
 }
 

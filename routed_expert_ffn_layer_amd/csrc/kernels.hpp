@@ -10,6 +10,9 @@ namespace moe {
 struct FfnArgs;
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st);
+// Top-k then permutation; one workgroup launch for small batches.
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_rows, int32_t* inv_rows, hipStream_t st);
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_rows, int32_t* inv_rows, hipStream_t st);
 hipError_t launch_combine(const float* rows, const float* w, const int32_t* inv, const float* shared, int T, int k,

@@ -25,13 +25,12 @@ __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
   return va > vb || (va == vb && ia < ib);
 }
 
+// Top-k of one token row (all 64 lanes of the wave take part); lane j < k writes
+// the j-th winner and its gate weight to ids_out[j], w_out[j].
 template <int EPL>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                   int32_t* __restrict__ ids, float* __restrict__ w) {
+__device__ __forceinline__ void topk_row(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids_out,
+                                         float* __restrict__ w_out) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // uniform per wave
-  const float* row = logits + (size_t)t * E;
   float v[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
@@ -73,9 +72,17 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    w[(size_t)t * k + lane] = ex / s;
+    ids_out[lane] = my_id;
+    w_out[lane] = ex / s;
   }
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                   int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // uniform per wave
+  topk_row<EPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st) {
@@ -103,12 +110,12 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 // ---------------------------------------------------------------------------
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
+constexpr int kRouteFusedMaxT = 64;  // batches routed by one workgroup launch
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ ids, int n, int E,
-                                                               int32_t* __restrict__ counts,
-                                                               int32_t* __restrict__ offsets,
-                                                               int32_t* __restrict__ sorted_rows,
-                                                               int32_t* __restrict__ inv_rows) {
+// The whole permutation, run by one workgroup of kPermThreads threads.
+__device__ __forceinline__ void permute_block(const int32_t* ids, int n, int E, int32_t* __restrict__ counts,
+                                              int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows,
+                                              int32_t* __restrict__ inv_rows) {
   __shared__ int s_base[1024];   // histogram, then exclusive offsets
   __shared__ int s_run[1024];    // pairs of each expert placed in earlier rounds
   __shared__ uint16_t s_wcnt[kPermWaves][1024];
@@ -172,6 +179,52 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ ids, int n, int E,
+                                                               int32_t* __restrict__ counts,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ sorted_rows,
+                                                               int32_t* __restrict__ inv_rows) {
+  permute_block(ids, n, E, counts, offsets, sorted_rows, inv_rows);
+}
+
+// Top-k and permutation in one workgroup launch (small batches): the 16 waves
+// take the tokens in turn, the barrier makes every token's ids visible to the
+// workgroup, then the permutation runs on them.  Same code as the two kernels,
+// so the same results.
+template <int EPL>
+__global__ __launch_bounds__(kPermThreads) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                             int32_t* __restrict__ ids, float* __restrict__ w,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted_rows,
+                                                             int32_t* __restrict__ inv_rows) {
+  for (int t = threadIdx.x >> 6; t < T; t += kPermWaves)
+    topk_row<EPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+  __syncthreads();
+  permute_block(ids, T * k, E, counts, offsets, sorted_rows, inv_rows);
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_rows, int32_t* inv_rows, hipStream_t st) {
+  if (T > kRouteFusedMaxT) {
+    hipError_t e = launch_topk(logits, T, E, k, ids, w, st);
+    if (e != hipSuccess) return e;
+    return launch_permute(ids, T, k, E, counts, offsets, sorted_rows, inv_rows, st);
+  }
+  const dim3 grid(1), block(kPermThreads);
+  if (E <= 64)
+    hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, st, logits, T, E, k, ids, w, counts, offsets, sorted_rows, inv_rows);
+  else if (E <= 128)
+    hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, st, logits, T, E, k, ids, w, counts, offsets, sorted_rows, inv_rows);
+  else if (E <= 256)
+    hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, st, logits, T, E, k, ids, w, counts, offsets, sorted_rows, inv_rows);
+  else if (E <= 512)
+    hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, st, logits, T, E, k, ids, w, counts, offsets, sorted_rows, inv_rows);
+  else
+    hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, st, logits, T, E, k, ids, w, counts, offsets, sorted_rows, inv_rows);
+  return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,

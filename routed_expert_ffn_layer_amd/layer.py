@@ -31,6 +31,7 @@ class LayerBuffers:
         self.ydt = moe.MOE_F32 if wdt == moe.MOE_F32 else moe.MOE_BF16
         self.y = torch.empty((T, H), dtype=f32 if self.ydt == moe.MOE_F32 else torch.bfloat16, device=dev)
         self.slot_table = torch.empty(E, dtype=i32, device=dev)
+        self.slot_misses = torch.empty(E, dtype=i32, device=dev)
 
 
 def identity_slots(E, device="cuda"):
@@ -39,8 +40,7 @@ def identity_slots(E, device="cuda"):
 
 
 def route(b: LayerBuffers, logits, stream=None):
-    moe.moe_route_topk(logits, b.k, b.topk_ids, b.topk_w, stream)
-    moe.moe_permute(b.topk_ids, b.E, b.counts, b.offsets, b.sorted_rows, b.inv_rows, stream)
+    moe.moe_route(logits, b.k, b.topk_ids, b.topk_w, b.counts, b.offsets, b.sorted_rows, b.inv_rows, stream)
 
 
 def ffn(b: LayerBuffers, x, slot_pool, slot_stride, slot_of_expert, shared_w=None, stream=None):
@@ -71,5 +71,26 @@ def forward_cached(b: LayerBuffers, cache: moe.MoeCache, layer, logits, x, slot_
     for w in range(1, stats["n_waves"]):
         waves.append(cache.lookup_fill(layer, None, w, b.slot_table, stream))
         ffn(b, x, slot_pool, slot_stride, b.slot_table, None, stream)
+    combine(b, shared_w is not None, stream)
+    return b.y, waves
+
+
+def forward_cached_split(b: LayerBuffers, cache: moe.MoeCache, layer, logits, x, slot_pool, slot_stride,
+                         shared_w=None, stream=None):
+    """As forward_cached, but each wave's resident experts are computed while its
+    misses are filled; the misses' FFN follows once their fills have landed."""
+    route(b, logits, stream)
+    waves = []
+    w = 0
+    while True:
+        stats = cache.lookup_fill_split(layer, b.counts if w == 0 else None, w, b.slot_table, b.slot_misses, stream)
+        waves.append(stats)
+        ffn(b, x, slot_pool, slot_stride, b.slot_table, shared_w if w == 0 else None, stream)
+        cache.wait_fills(stream)
+        if stats["fill_bytes"]:
+            ffn(b, x, slot_pool, slot_stride, b.slot_misses, None, stream)
+        w += 1
+        if w >= stats["n_waves"]:
+            break
     combine(b, shared_w is not None, stream)
     return b.y, waves

@@ -53,6 +53,7 @@ class LayerStreamDesc(ctypes.Structure):
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_last_error", "moe_expert_bytes", "moe_route_topk",
            "moe_permute", "moe_cache_create", "moe_cache_destroy", "moe_cache_lookup_fill",
            "moe_cache_lookup_host", "moe_cache_state", "moe_cache_inject_fill_failure",
+           "moe_cache_lookup_fill_split", "moe_cache_wait_fills", "moe_route",
            "moe_grouped_ffn_workspace", "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down",
            "moe_combine", "moe_layer_stream_create", "moe_layer_stream_destroy", "moe_layer_stream_fill",
            "moe_layer_stream_acquire", "moe_layer_stream_release"]
@@ -75,10 +76,13 @@ def lib():
     L.moe_expert_bytes.argtypes = [i, i, i]
     L.moe_route_topk.argtypes = [P, i, i, i, P, P, P]
     L.moe_permute.argtypes = [P, i, i, i, P, P, P, P, P]
+    L.moe_route.argtypes = [P, i, i, i, P, P, P, P, P, P, P]
     L.moe_cache_create.argtypes = [ctypes.POINTER(CacheDesc), ctypes.POINTER(P)]
     L.moe_cache_destroy.argtypes = [P]
     L.moe_cache_lookup_fill.argtypes = [P, i, P, i, P, ctypes.POINTER(CacheStats), P]
     L.moe_cache_lookup_host.argtypes = [P, i, P, i, P, P, i, ctypes.POINTER(i), ctypes.POINTER(CacheStats)]
+    L.moe_cache_lookup_fill_split.argtypes = [P, i, P, i, P, P, ctypes.POINTER(CacheStats), P]
+    L.moe_cache_wait_fills.argtypes = [P, P]
     L.moe_cache_state.argtypes = [P, P, P]
     L.moe_cache_inject_fill_failure.argtypes = [P, ctypes.c_int64]
     L.moe_grouped_ffn_workspace.restype = sz
@@ -126,6 +130,12 @@ def moe_expert_bytes(wdt, H, I):
 def moe_route_topk(logits, k, topk_ids, topk_w, stream=None):
     T, E = logits.shape
     _check(lib().moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
+
+
+def moe_route(logits, k, topk_ids, topk_w, counts, offsets, sorted_rows, inv_rows, stream=None):
+    T, E = logits.shape
+    _check(lib().moe_route(_ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets),
+                           _ptr(sorted_rows), _ptr(inv_rows), _stream(stream)))
 
 
 def moe_permute(topk_ids, E, counts, offsets, sorted_rows, inv_rows, stream=None):
@@ -202,6 +212,15 @@ class MoeCache:
         _check(lib().moe_cache_lookup_fill(self._h, layer, _ptr(counts), wave, _ptr(slot_of_expert),
                                            ctypes.byref(st), _stream(stream)))
         return st.as_dict()
+
+    def lookup_fill_split(self, layer, counts, wave, slot_hits, slot_misses, stream=None):
+        st = CacheStats()
+        _check(lib().moe_cache_lookup_fill_split(self._h, layer, _ptr(counts), wave, _ptr(slot_hits),
+                                                 _ptr(slot_misses), ctypes.byref(st), _stream(stream)))
+        return st.as_dict()
+
+    def wait_fills(self, stream=None):
+        _check(lib().moe_cache_wait_fills(self._h, _stream(stream)))
 
     def lookup_host(self, layer, counts_host, wave):
         """counts_host: numpy int32 [E] (ignored for wave > 0).  Returns (slot table, fills, stats)."""

@@ -86,9 +86,11 @@ def test_tiny_layer_two_waves_and_single_token_steps(ora):
     cache.close()
 
 
-def test_cached_trace_bitwise_equal_to_resident(ora):
+@pytest.mark.parametrize("split", [False, True], ids=["whole", "split"])
+def test_cached_trace_bitwise_equal_to_resident(ora, split):
     """Temporally correlated trace (reuse 0.7, Zipf 1.0) through a 37%-capacity
-    cache over 6 layers, bf16 experts with a reduced hidden size."""
+    cache over 6 layers, bf16 experts with a reduced hidden size; whole waves, or
+    hits computed while the misses fill (split lookup)."""
     H, I, E, k, Ls, tokens = 256, 128, 64, 8, 6, 30
     S = int(0.37 * Ls * E)
     seed = 1005
@@ -108,7 +110,8 @@ def test_cached_trace_bitwise_equal_to_resident(ora):
         for l in range(Ls):
             lg_d = to_dev(lg[t, l][None, :])
             y_ref = _resident_y(b, lg_d, x, resident[l * E:(l + 1) * E], eb, E)
-            y, waves = L.forward_cached(bc, cache, l, lg_d, x, slot_pool, stride)
+            fwd = L.forward_cached_split if split else L.forward_cached
+            y, waves = fwd(bc, cache, l, lg_d, x, slot_pool, stride)
             torch.cuda.synchronize()
             assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), (t, l)
             r = lru.step(l, bc.counts.cpu().numpy())
@@ -117,6 +120,36 @@ def test_cached_trace_bitwise_equal_to_resident(ora):
             total["misses"] += waves[0]["misses"]
     _same_state(cache, lru)
     log(f"trace miss rate {total['misses'] / total['accesses']:.3f}")
+    cache.close()
+
+
+def test_split_lookup_waves_and_shared_expert(ora):
+    """Split lookups over several waves (16 active experts, 6 slots) with a shared
+    expert: every step equals the resident layer bit for bit and the cache state
+    equals the oracle's LRU."""
+    H, I, E, k, S, T = 128, 64, 16, 4, 6, 12
+    lay = synth.small_layer(synth.BF16, T, H, I, E, k, seed=78, shared=True, I_shared=64)
+    eb = lay["experts"].shape[1]
+    host = _pinned_pool(lay["experts"])
+    cache, slot_pool, stride = _device_cache(1, E, S, eb, host)
+    lru = ora.LRU(S, 1, E)
+    resident = to_dev(lay["experts"])
+    shared = to_dev(lay["shared"])
+    b = L.LayerBuffers(T, E, k, H, I, synth.BF16, I_shared=64)
+    bc = L.LayerBuffers(T, E, k, H, I, synth.BF16, I_shared=64)
+    for step in range(3):
+        x_d = to_dev(synth.encode_activations(synth.BF16, synth.normal_x(78, T, H, step)))
+        lg_d = to_dev(synth.normal_logits(78, T, E, step))
+        L.forward(b, lg_d, x_d, resident, eb, L.identity_slots(E), shared)
+        torch.cuda.synchronize()
+        y_ref = b.y.clone()
+        y, waves = L.forward_cached_split(bc, cache, 0, lg_d, x_d, slot_pool, stride, shared)
+        torch.cuda.synchronize()
+        assert waves[0]["n_waves"] >= 2
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), step
+        r = lru.step(0, bc.counts.cpu().numpy())
+        assert r["n_waves"] == waves[0]["n_waves"]
+        _same_state(cache, lru)
     cache.close()
 
 

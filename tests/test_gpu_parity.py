@@ -52,6 +52,45 @@ def test_topk_matches_oracle(ora, case):
     np.testing.assert_allclose(w, rw, rtol=W_RTOL, atol=W_ATOL)
 
 
+@pytest.mark.parametrize("T,k,E", [(0, 4, 16), (1, 8, 256), (8, 6, 256), (64, 16, 1024), (65, 6, 256), (17, 2, 8),
+                                   (300, 8, 256), (5, 1, 1), (40, 3, 100)])
+def test_route_fused_matches_separate_calls_and_oracle(ora, T, k, E):
+    """moe_route (one workgroup launch up to 64 tokens) = moe_route_topk + moe_permute
+    bit for bit, and the oracle's routing and permutation; logits rounded to a
+    coarse grid so that ties occur."""
+    log(f"route T={T} k={k} E={E}")
+    g = np.random.default_rng(900 + T + E)
+    logits = (np.round(g.standard_normal((T, E)) * 4) / 4).astype(np.float32)
+    lg = to_dev(logits) if T else torch.zeros((0, E), dtype=torch.float32, device=dev())
+    n = max(T * k, 1)
+
+    def bufs():
+        return (torch.full((max(T, 1), k), -7, dtype=torch.int32, device=dev()),
+                torch.zeros((max(T, 1), k), dtype=torch.float32, device=dev()),
+                torch.full((E,), -7, dtype=torch.int32, device=dev()),
+                torch.full((E + 1,), -7, dtype=torch.int32, device=dev()),
+                torch.full((n,), -7, dtype=torch.int32, device=dev()),
+                torch.full((n,), -7, dtype=torch.int32, device=dev()))
+
+    a, b = bufs(), bufs()
+    moe.moe_route(lg, k, *a)
+    if T:
+        moe.moe_route_topk(lg, k, b[0], b[1])
+    moe.moe_permute(b[0][:T], E, b[2], b[3], b[4], b[5])
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    if T:
+        rids, _, rw = ora.route_topk(logits, k)
+        np.testing.assert_array_equal(a[0].cpu().numpy(), rids)
+        np.testing.assert_allclose(a[1].cpu().numpy(), rw, rtol=W_RTOL, atol=W_ATOL)
+        rc, ro, rs, ri = ora.permute(rids, E)
+        np.testing.assert_array_equal(a[2].cpu().numpy(), rc)
+        np.testing.assert_array_equal(a[3].cpu().numpy(), ro)
+        np.testing.assert_array_equal(a[4].cpu().numpy()[:T * k], rs)
+        np.testing.assert_array_equal(a[5].cpu().numpy()[:T * k], ri)
+
+
 @pytest.mark.parametrize("T,k,E", [(0, 4, 16), (1, 8, 256), (16, 8, 256), (32, 2, 8), (4096, 6, 256), (3, 1, 1),
                                    (1000, 32, 1024), (777, 5, 300)])
 def test_permute_matches_oracle(ora, T, k, E):
