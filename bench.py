@@ -63,6 +63,9 @@ def parse():
                     help="distinct layers kept in pinned host memory (layer l reads host layer l mod this)")
     ap.add_argument("--distinct-experts", type=int, default=512,
                     help="decode_mxfp4: distinct generated experts copied into the 11,008 slots")
+    ap.add_argument("--eager", action="store_true",
+                    help="decode workloads: launch every call from Python each step (default: one captured HIP "
+                         "graph per step, replayed)")
     ap.add_argument("--split-waves", action="store_true",
                     help="cached_trace_bf16: compute each wave's hits while its misses fill (default: after all fills)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
@@ -222,7 +225,23 @@ def layer_bytes(wdt, n_experts_active, has_shared, T, k, E, H, I):
 # ---------------------------------------------------------------------------
 # decode_bf16 (the headline workload).
 
-def run_decode_bf16(T, n_layers, steps, warmup, time_kernel=True):
+def replay_step(step, eager):
+    """The step as given (eager), or captured once into a HIP graph and replayed:
+    a decode step over resident experts has no host synchronisation, so its
+    launches are recorded once (after one eager run that loads the kernels)."""
+    if eager:
+        return step
+    import torch
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    return graph.replay
+
+
+def run_decode_bf16(T, n_layers, steps, warmup, time_kernel=True, eager=False):
     import torch
     import synth
     from routed_expert_ffn_layer_amd import layer as L
@@ -253,12 +272,13 @@ def run_decode_bf16(T, n_layers, steps, warmup, time_kernel=True):
                                      b.sorted_rows, T, k, E, H, I, b.out_rows, b.shared_out, b.workspace)
             L.combine(b, True)
 
+    run = replay_step(step, eager)
     for _ in range(warmup):
-        step()
+        run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step()
+        run()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     active = [int((b.counts > 0).sum().item()) for b in bufs]
@@ -321,14 +341,14 @@ def workload_decode_bf16(args):
     n_layers = args.layers or 16
     steps, warmup = args.steps or 50, 5 if args.warmup is None else args.warmup
     extra = [int(v) for v in ("1,4" if args.extra_batches is None else args.extra_batches).split(",") if v.strip()]
-    main_res = run_decode_bf16(T, n_layers, steps, warmup)
+    main_res = run_decode_bf16(T, n_layers, steps, warmup, eager=args.eager)
     keys = ("layer_tokens_per_s", "ms_per_step", "layer_hbm_gbs", "gate_up_gbs", "gate_up_avg_us",
             "active_experts_mean")
     by_batch = {str(T): {k: main_res[k] for k in keys}}
     for tb in extra:
         if tb == T:
             continue
-        r = run_decode_bf16(tb, n_layers, max(10, steps // 2), 2)
+        r = run_decode_bf16(tb, n_layers, max(10, steps // 2), 2, eager=args.eager)
         by_batch[str(tb)] = {k: r[k] for k in keys}
     cpu = None if args.no_cpu_baseline else cpu_decode_bf16(args.cpu_seconds)
     achieved = main_res["gate_up_gbs"]
@@ -337,7 +357,8 @@ def workload_decode_bf16(args):
         "synthetic (seeded N(0,0.02) weights, N(0,1) logits and activations)",
         {"workload": "decode layer bf16: hidden 2048, 256 routed experts + 1 shared, top-8, intermediate 512",
          "tokens_per_layer": T, "stacked_layers": n_layers,
-         "weights_in_hbm_gb": round(n_layers * 257 * 6291456 / 1e9, 2), "slots": "all resident"},
+         "weights_in_hbm_gb": round(n_layers * 257 * 6291456 / 1e9, 2), "slots": "all resident",
+         "launch": "eager" if args.eager else "one HIP graph per step"},
         {"kernel": "gate_up_mfma<bf16> (moe_grouped_ffn_gate_up)", "bound": "hbm", "achieved": achieved,
          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("decode_bf16"),
          "avg_launch_us": main_res["gate_up_avg_us"], "algorithmic_bytes_per_launch": main_res["gate_up_bytes_avg"],
@@ -373,7 +394,7 @@ def mxfp4_resident_stack(c, n_layers, n_distinct, dev):
     return stack, distinct
 
 
-def run_decode_mxfp4(stack, c, T, n_layers, steps, warmup, n_batches=4):
+def run_decode_mxfp4(stack, c, T, n_layers, steps, warmup, n_batches=4, eager=False):
     import torch
     import synth
     from routed_expert_ffn_layer_amd import layer as L
@@ -394,12 +415,14 @@ def run_decode_mxfp4(stack, c, T, n_layers, steps, warmup, n_batches=4):
         for l in range(n_layers):
             L.forward(bufs[l], logits[l][bi], xs[bi], pools[l], eb, slots)
 
+    # one captured step per batch (the batches are different input buffers)
+    runs = [replay_step(lambda bi=bi: step(bi), eager) for bi in range(n_batches)]
     for j in range(warmup):
-        step(j)
+        runs[j % n_batches]()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j in range(steps):
-        step(j)
+        runs[j % n_batches]()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     # routing of every (layer, batch), for the algorithmic bytes of the timed steps
@@ -483,7 +506,8 @@ def workload_decode_mxfp4(args):
     res = {}
     for tb in batches:
         progress(f"decode_mxfp4: T={tb}")
-        res[tb] = run_decode_mxfp4(stack, c, tb, n_layers, steps if tb == T else max(4, steps // 2), warmup)
+        res[tb] = run_decode_mxfp4(stack, c, tb, n_layers, steps if tb == T else max(4, steps // 2), warmup,
+                                   eager=args.eager)
     cpu = None if args.no_cpu_baseline else cpu_decode_mxfp4(stack, c, 8, args.cpu_seconds)
     m = res[T]
     keys = ("layer_tokens_per_s", "stack_tokens_per_s", "ms_per_step", "layer_hbm_gbs", "gate_up_gbs",
@@ -494,7 +518,8 @@ def workload_decode_mxfp4(args):
         "into every slot; Zipf(1.1) popularity + N(0,1) logits, 4 batches per layer cycled; N(0,1) activations)",
         {"workload": "decode layer MXFP4: hidden 4096, 256 routed experts, top-6, intermediate 2048",
          "tokens_per_layer": T, "stacked_layers": n_layers,
-         "weights_in_hbm_gb": round(stack.numel() / 1e9, 2), "slots": "all resident"},
+         "weights_in_hbm_gb": round(stack.numel() / 1e9, 2), "slots": "all resident",
+         "launch": "eager" if args.eager else "one HIP graph per step"},
         {"kernel": "gate_up_mfma<mxfp4> (moe_grouped_ffn_gate_up)", "bound": "hbm", "achieved": m["gate_up_gbs"],
          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": m["gate_up_gbs"] / HBM_PEAK_GBS,
          "traffic": measured_traffic("decode_mxfp4"),
