@@ -121,10 +121,17 @@ __global__ __launch_bounds__(256) void down_f32(FfnArgs a, int shared_tiles, int
 #ifndef MOE_DEC_MXN_DIV
 #define MOE_DEC_MXN_DIV 2
 #endif
-template <int WT, int NT>
+#ifndef MOE_DEC_RING
+#define MOE_DEC_RING 4
+#endif
+#ifndef MOE_DEC_LB_WAVES
+#define MOE_DEC_LB_WAVES 3
+#endif
+constexpr int kDecRing = MOE_DEC_RING;  // weight steps in flight per wave (token rows in LDS)
+template <int WT, int NT, bool LB = false>
 struct DecTune {
   static constexpr bool mx = WT == W_MXFP4, mx1 = mx && NT == 1;
-  static constexpr int waves = mx1 ? MOE_DEC_MX1_WAVES : mx ? MOE_DEC_MXN_WAVES : 1;
+  static constexpr int waves = mx && LB ? MOE_DEC_LB_WAVES : mx1 ? MOE_DEC_MX1_WAVES : mx ? MOE_DEC_MXN_WAVES : 1;
   static constexpr int div = mx1 ? MOE_DEC_MX1_DIV : mx ? MOE_DEC_MXN_DIV : 1;
 };
 // k steps per chunk of loads (bounded by the registers two chunks take).
@@ -257,6 +264,67 @@ __device__ __forceinline__ void mfma_rows(const Mat& w, const int (&atile)[R], i
   constexpr int U = Unroll<WT, NT, R>::value;
   if (s0 >= s1) return;
   Chunk<WT, NT, R, U> c0, c1;
+  if constexpr (WT == W_MXFP4 && LB) {
+    // Token rows in LDS, so weight fragments are the only vector-memory loads:
+    // a ring of kDecRing column steps per wave keeps that many steps of weights
+    // in flight (step s requests step s + kDecRing - 1 into the slot step s - 1
+    // has just used); scale blocks a block ahead as below.  The body is unrolled
+    // over 16-step blocks, so ring slots and scale bytes are fixed positions.
+    static_assert(16 % kDecRing == 0, "ring slots tile a scale block");
+    if (s0 % 16 == 0 && (s1 - s0) % 16 == 0 && w.K % 128 == 0) {
+      const int lane = threadIdx.x & 63, g = lane >> 4;
+      const int nb = (s1 - s0) / 16;
+      u32x4 ring[kDecRing][R];
+      u32x4 sb[2][R];
+      auto load_sb = [&](u32x4(&dst)[R], int step) {
+#pragma unroll
+        for (int t = 0; t < R; ++t) dst[t] = load_scale_block(w, lane, atile[t], step);
+      };
+      auto load_a = [&](u32x4(&dst)[R], int step) {
+#pragma unroll
+        for (int t = 0; t < R; ++t) dst[t] = bld16(w.codes, lane * 16, (atile[t] * w.nK + step) * 1024);
+      };
+      auto compute = [&](const u32x4(&a)[R], const u32x4(&sbk)[R], int sofs, int s) {
+        bf16x8 B[NT][4];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            B[nt][m] = as_bf16x8(*reinterpret_cast<const u32x4*>(rows.lds + brow[nt] * rows.lds_ld +
+                                                                 (s * 128 + 32 * g + 8 * m) * 2));
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+          const float sc = scale_of_word(sbk[t][sofs / 4], sofs);
+          bf16x8 A[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) A[m] = fp4x8_to_bf16x8(a[t][m], sc);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            if (nt < ntl)
+#pragma unroll
+              for (int m = 0; m < 4; ++m)
+                acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m], B[nt][m], acc[t][nt], 0, 0, 0);
+        }
+      };
+      auto block = [&](u32x4(&cur)[R], u32x4(&next)[R], int sblk) {
+        load_sb(next, min(sblk + 16, s1 - 16));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          load_a(ring[(i + kDecRing - 1) % kDecRing], min(sblk + i + kDecRing - 1, s1 - 1));
+          __builtin_amdgcn_sched_barrier(0);  // keep the request ahead of this step's work
+          compute(ring[i % kDecRing], cur, i, sblk + i);
+        }
+      };
+      load_sb(sb[0], s0);
+#pragma unroll
+      for (int d = 0; d < kDecRing - 1; ++d) load_a(ring[d], min(s0 + d, s1 - 1));
+      for (int b = 0; b < nb; b += 2) {
+        block(sb[0], sb[1], s0 + 16 * b);
+        if (b + 1 < nb) block(sb[1], sb[0], s0 + 16 * (b + 1));
+      }
+      return;
+    }
+  }
   if constexpr (WT == W_MXFP4) {
     // Whole 16-step scale blocks: one 16-byte scale load per lane and row tile
     // per block, issued a block ahead (two register sets, so the unrolled body
@@ -337,7 +405,7 @@ __device__ __forceinline__ void stage_rows(uint8_t* lds, const uint16_t* src, in
 // 16-row A tile = gate rows j..j+7 stacked on up rows j..j+7, so the epilogue
 // pairs lane l (gate) with lane l+32 (up) and writes h = SiLU(gate) * up as bf16.
 template <int WT, int NT, int KW, int R, bool LB = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT, NT>::waves))) void gate_up_mfma(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT, NT, LB>::waves))) void gate_up_mfma(
     FfnArgs a, int shared_tiles, int routed_tiles) {
   constexpr int RT = 4 / KW;
   const Item it = resolve_item(a, shared_tiles, routed_tiles);
@@ -447,7 +515,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
 
 // down: row tile t of a wave is 16 output columns (rows of W2) of one item.
 template <int WT, int NT, int KW, int R, bool LB = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT, NT>::waves))) void down_mfma(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT, NT, LB>::waves))) void down_mfma(
     FfnArgs a, int shared_tiles, int routed_tiles) {
   constexpr int RT = 4 / KW;
   const Item it = resolve_item(a, shared_tiles, routed_tiles);
@@ -593,7 +661,7 @@ static int pick_nt(int T, int wtype) {
 #define MOE_DEC_LDS_ROWS_MAX 65536
 #endif
 #ifndef MOE_DEC_LDS_MIN_T
-#define MOE_DEC_LDS_MIN_T 4
+#define MOE_DEC_LDS_MIN_T 1
 #endif
 static size_t lds_rows_bytes(int T, int K) {
   return T < MOE_DEC_LDS_MIN_T ? (size_t)-1 : (size_t)(T < 16 ? T : 16) * ((size_t)K * 2 + 16);
