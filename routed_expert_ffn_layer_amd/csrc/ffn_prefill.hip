@@ -40,6 +40,13 @@ constexpr int kPfDepth = 4;                         // buffers / register sets
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// 1 KB pieces (4 token rows of a chunk) each wave writes per chunk: 4*NTL pieces
+// spread over the WAVES waves.
+template <int NTL, int WAVES>
+struct PfPieces {
+  static constexpr int value = (4 * NTL + WAVES - 1) / WAVES;
+};
+
 template <int WT, int R, int U>
 struct AChunk {
   u32x4 qa[U][R];
@@ -158,24 +165,23 @@ struct PfBufs {
 // tile t of unit u for this wave; epi(u, t, nt, acc) stores a result tile.
 template <int WT, int NTL, int R, int WAVES, typename ATileOf, typename Epi>
 __device__ __forceinline__ void prefill_units(const Mat& w, int nu, const ATileOf& atile_of,
-                                              __amdgpu_buffer_rsrc_t src, const int (&voff)[(NTL + 1) / 2],
+                                              __amdgpu_buffer_rsrc_t src, const int (&voff)[PfPieces<NTL, WAVES>::value],
                                               const PfBufs& bufs, const Epi& epi) {
-  static_assert(WAVES == 8, "the B pieces are spread over 8 waves");
   constexpr int U = kPfKC / KStep<WT>::value;
-  constexpr int PW = (NTL + 1) / 2;                         // B pieces per wave
+  constexpr int PW = PfPieces<NTL, WAVES>::value;            // B pieces per wave
   constexpr int NL = PW + R * U * (WT == W_MXFP4 ? 2 : 1);  // vector loads per chunk
   const int wv = uniform(threadIdx.x >> 6);
   const int nchunks = w.K / kPfKC, lastf = nu * nchunks - 1;
   AChunk<WT, R, U> a[kPfDepth];
   f32x4 acc[R][NTL];
-  // Token rows of a chunk: wave wv writes the 1 KB pieces P = 8*i + wv (token rows
+  // Token rows of a chunk: wave wv writes the 1 KB pieces P = WAVES*i + wv (token rows
   // 4P..4P+3), i < PW; lane l fills position l % 16 of row 4P + l / 16.  voff[i]
   // holds the lane's row start plus its swizzled piece offset.  The weights come
   // from the unit's row tiles.
   auto issue = [&](int set, int f) {
     const int u = f / nchunks, ch = f - u * nchunks;
 #pragma unroll
-    for (int i = 0; i < PW; ++i) dma16(src, voff[i], ch * kPfRowBytes, bufs.b[set] + (8 * i + wv) * 1024);
+    for (int i = 0; i < PW; ++i) dma16(src, voff[i], ch * kPfRowBytes, bufs.b[set] + (WAVES * i + wv) * 1024);
     int at[R];
 #pragma unroll
     for (int t = 0; t < R; ++t) at[t] = atile_of(u, t);
@@ -243,12 +249,12 @@ template <int WT, int NTL, int R, int WAVES, typename RowStart, typename ATileOf
 __device__ __forceinline__ void prefill_pass(const Mat& w, int nu, const ATileOf& atile_of,
                                              __amdgpu_buffer_rsrc_t src, const RowStart& row_start,
                                              const PfBufs& bufs, const Epi& epi) {
-  constexpr int PW = (NTL + 1) / 2;
+  constexpr int PW = PfPieces<NTL, WAVES>::value;
   const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
   int voff[PW];
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
-    const int row = 4 * (8 * i + wv) + (lane >> 4);
+    const int row = 4 * (WAVES * i + wv) + (lane >> 4);
     voff[i] = row_start(row) + (((lane & 15) ^ (row & 15)) << 4);
   }
   prefill_units<WT, NTL, R, WAVES>(w, nu, atile_of, src, voff, bufs, epi);
@@ -366,9 +372,15 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_down(FfnArgs a, PfGrid gr)
 // Launch: 8 waves and 128 KB of LDS; R row tiles per wave: 2 for MXFP4 (four
 // register sets of 2 x 80 bytes per lane), 1 for bf16 (a bf16 chunk is four column
 // steps, so one row tile already holds 4 x 16 bytes per set).
-constexpr int kPfWaves = 8;
+#ifndef MOE_PF_WAVES
+#define MOE_PF_WAVES 8
+#endif
+#ifndef MOE_PF_R_MX
+#define MOE_PF_R_MX 2
+#endif
+constexpr int kPfWaves = MOE_PF_WAVES;
 template <int WT>
-constexpr int pf_r() { return WT == W_MXFP4 ? 2 : 1; }
+constexpr int pf_r() { return WT == W_MXFP4 ? MOE_PF_R_MX : 1; }
 
 bool prefill_supported(int wtype, int H, int I, int I_shared) {
   if (wtype != W_BF16 && wtype != W_MXFP4) return false;
