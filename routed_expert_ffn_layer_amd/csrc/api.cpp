@@ -213,7 +213,12 @@ int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, 
   a.routed_items = (int)((int64_t)T * k < E ? (int64_t)T * k : E);
   // Prefill-sized batches (32 or more pairs per expert on average) take the
   // LDS-staged kernels; the results are the same computation.
-  const bool prefill = (int64_t)T * k >= (int64_t)32 * E && moe::prefill_supported(wdt, H, I, I_shared);
+  // LDS-staged prefill kernels once experts carry MOE_PF_MIN_PAIRS token pairs on average.
+#ifndef MOE_PF_MIN_PAIRS
+#define MOE_PF_MIN_PAIRS 32
+#endif
+  const bool prefill =
+      (int64_t)T * k >= (int64_t)MOE_PF_MIN_PAIRS * E && moe::prefill_supported(wdt, H, I, I_shared);
   if (phases & PHASE_GATE_UP) {
     hipError_t e = prefill ? moe::launch_prefill_gate_up(wdt, a, stream) : moe::launch_ffn_gate_up(wdt, a, stream);
     if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn gate_up launch");
