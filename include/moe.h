@@ -107,7 +107,7 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, i
                 int32_t* sorted_rows, int32_t* inv_rows, hipStream_t stream);
 
 /* moe_route_topk followed by moe_permute on the same buffers, with the same
- * arguments, requirements and results; batches of at most 64 tokens run as one
+ * arguments, requirements and results; batches of at most 8 tokens run as one
  * workgroup launch (one launch fewer per decode layer). */
 int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w, int32_t* counts,
               int32_t* offsets, int32_t* sorted_rows, int32_t* inv_rows, hipStream_t stream);

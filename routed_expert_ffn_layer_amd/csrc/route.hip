@@ -110,7 +110,7 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 // ---------------------------------------------------------------------------
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
-constexpr int kRouteFusedMaxT = 64;  // batches routed by one workgroup launch
+constexpr int kRouteFusedMaxT = 8;  // batches routed by one workgroup launch (measured: wins up to 8)
 
 // The whole permutation, run by one workgroup of kPermThreads threads.
 __device__ __forceinline__ void permute_block(const int32_t* ids, int n, int E, int32_t* __restrict__ counts,
