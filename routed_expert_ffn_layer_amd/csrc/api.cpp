@@ -211,6 +211,7 @@ int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, 
   a.I_shared = I_shared;
   a.h_ld = I > I_shared ? I : I_shared;
   a.routed_items = (int)((int64_t)T * k < E ? (int64_t)T * k : E);
+  a.lds_rows = 0;  // set per launch by the decode launchers
   // Prefill-sized batches (32 or more pairs per expert on average) take the
   // LDS-staged kernels; the results are the same computation.
   // LDS-staged prefill kernels once experts carry MOE_PF_MIN_PAIRS token pairs on average.

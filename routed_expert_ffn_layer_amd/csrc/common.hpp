@@ -31,6 +31,7 @@ struct FfnArgs {
   int T, k, E, H, I, I_shared;
   int h_ld;                       // row stride of h in elements (max(I, I_shared))
   int routed_items;               // grid slots for routed experts: min(E, T*k)
+  int lds_rows;                   // token rows the launch's dynamic LDS holds (0: none)
 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }

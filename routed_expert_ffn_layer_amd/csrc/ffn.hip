@@ -439,17 +439,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
       const int i = min(pass + nt * 16 + r, it.n - 1);  // padding columns re-read a real row
       xrow[nt] = item_token(a, it, i);
     }
+    bool staged = false;  // uniform per block: this pass's token rows are in LDS
     if constexpr (LB) {
       extern __shared__ __attribute__((aligned(16))) uint8_t lds_rows[];
       const int np = min(NT * 16, it.n - pass);
+      staged = np <= a.lds_rows;
       if (pass > 0) __syncthreads();  // the previous pass has finished reading
-      stage_rows(lds_rows, reinterpret_cast<const uint16_t*>(a.x), np, H,
-                 [&](int i) { return (size_t)item_token(a, it, pass + i) * H; });
+      if (staged)
+        stage_rows(lds_rows, reinterpret_cast<const uint16_t*>(a.x), np, H,
+                   [&](int i) { return (size_t)item_token(a, it, pass + i) * H; });
       __syncthreads();
-      rows.lds = lds_rows;
-      rows.lds_ld = H * 2 + 16;
+      if (staged) {
+        rows.lds = lds_rows;
+        rows.lds_ld = H * 2 + 16;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) xrow[nt] = min(nt * 16 + r, np - 1);
+        for (int nt = 0; nt < NT; ++nt) xrow[nt] = min(nt * 16 + r, np - 1);
+      }
     }
     f32x4 acc[R][NT];
 #pragma unroll
@@ -457,7 +462,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (ntiles == R) {
-      mfma_rows<WT, NT, R, LB>(w, atile, s0, s1, g, rows, xrow, ntl, acc);
+      if (staged)
+        mfma_rows<WT, NT, R, LB>(w, atile, s0, s1, g, rows, xrow, ntl, acc);
+      else
+        mfma_rows<WT, NT, R, false>(w, atile, s0, s1, g, rows, xrow, ntl, acc);
     } else if (ntiles > 0) {
       // ragged last tiles of the item: one tile at a time
       for (int t = 0; t < ntiles; ++t) {
@@ -465,7 +473,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) one[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int tile1[1] = {j0 / 8 + t};
-        mfma_rows<WT, NT, 1, LB>(w, tile1, s0, s1, g, rows, xrow, ntl, one);
+        if (staged)
+          mfma_rows<WT, NT, 1, LB>(w, tile1, s0, s1, g, rows, xrow, ntl, one);
+        else
+          mfma_rows<WT, NT, 1, false>(w, tile1, s0, s1, g, rows, xrow, ntl, one);
 #pragma unroll
         for (int tt = 0; tt < R; ++tt)
           if (tt == t)
@@ -543,17 +554,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
       const int i = min(pass + nt * 16 + r, it.n - 1);  // padding columns re-read a real row
       hrow[nt] = it.hrow0 + i;
     }
+    bool staged = false;  // uniform per block: this pass's token rows are in LDS
     if constexpr (LB) {
       extern __shared__ __attribute__((aligned(16))) uint8_t lds_rows[];
       const int np = min(NT * 16, it.n - pass);
+      staged = np <= a.lds_rows;
       if (pass > 0) __syncthreads();  // the previous pass has finished reading
-      stage_rows(lds_rows, reinterpret_cast<const uint16_t*>(a.h), np, Ie,
-                 [&](int i) { return (size_t)(it.hrow0 + pass + i) * a.h_ld; });
+      if (staged)
+        stage_rows(lds_rows, reinterpret_cast<const uint16_t*>(a.h), np, Ie,
+                   [&](int i) { return (size_t)(it.hrow0 + pass + i) * a.h_ld; });
       __syncthreads();
-      rows.lds = lds_rows;
-      rows.lds_ld = Ie * 2 + 16;
+      if (staged) {
+        rows.lds = lds_rows;
+        rows.lds_ld = Ie * 2 + 16;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) hrow[nt] = min(nt * 16 + r, np - 1);
+        for (int nt = 0; nt < NT; ++nt) hrow[nt] = min(nt * 16 + r, np - 1);
+      }
     }
     f32x4 acc[R][NT];
 #pragma unroll
@@ -564,14 +580,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
       int atile[R];
 #pragma unroll
       for (int t = 0; t < R; ++t) atile[t] = row0 / 16 + t;
-      mfma_rows<WT, NT, R, LB>(w, atile, s0, s1, g, rows, hrow, ntl, acc);
+      if (staged)
+        mfma_rows<WT, NT, R, LB>(w, atile, s0, s1, g, rows, hrow, ntl, acc);
+      else
+        mfma_rows<WT, NT, R, false>(w, atile, s0, s1, g, rows, hrow, ntl, acc);
     } else if (ntiles > 0) {
       for (int t = 0; t < ntiles; ++t) {
         f32x4 one[1][NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) one[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int tile1[1] = {row0 / 16 + t};
-        mfma_rows<WT, NT, 1, LB>(w, tile1, s0, s1, g, rows, hrow, ntl, one);
+        if (staged)
+          mfma_rows<WT, NT, 1, LB>(w, tile1, s0, s1, g, rows, hrow, ntl, one);
+        else
+          mfma_rows<WT, NT, 1, false>(w, tile1, s0, s1, g, rows, hrow, ntl, one);
 #pragma unroll
         for (int tt = 0; tt < R; ++tt)
           if (tt == t)
@@ -640,8 +662,14 @@ static Shape gate_up_shape(int wtype, int T) {
   if (wtype == W_BF16) return T <= 4 ? Shape{4, 1} : Shape{2, 1};
   return T <= 16 ? Shape{1, MOE_DEC_MX1_R} : Shape{1, MOE_DEC_MXN_R};
 }
+#ifndef MOE_DEC_BF16_DN_KW
+#define MOE_DEC_BF16_DN_KW 1
+#endif
+#ifndef MOE_DEC_BF16_DN_R
+#define MOE_DEC_BF16_DN_R 2
+#endif
 static Shape down_shape(int wtype, int T) {
-  if (wtype == W_BF16) return Shape{1, 2};
+  if (wtype == W_BF16) return Shape{MOE_DEC_BF16_DN_KW, MOE_DEC_BF16_DN_R};
   return T <= 16 ? Shape{1, MOE_DEC_MX1_R} : Shape{1, MOE_DEC_MXN_R};
 }
 
@@ -654,25 +682,30 @@ static int pick_nt(int T, int wtype) {
 }
 
 // MXFP4 passes of one token tile take their token rows from LDS (staged once per
-// pass and block) when the batch has at least MOE_DEC_LDS_MIN_T tokens (below, the
-// staging costs more than it saves) and min(T, 16) rows of K columns fit in
-// MOE_DEC_LDS_ROWS_MAX bytes (above, LDS would cap the blocks per CU).
+// pass and block): the launch's dynamic LDS holds as many rows of K columns as fit
+// in MOE_DEC_LDS_ROWS_MAX bytes (more would cap the blocks per CU), at most
+// min(T, 16); a block whose pass has more rows reads them from memory instead.
 #ifndef MOE_DEC_LDS_ROWS_MAX
-#define MOE_DEC_LDS_ROWS_MAX 65536
+#define MOE_DEC_LDS_ROWS_MAX 49152
 #endif
 #ifndef MOE_DEC_LDS_MIN_T
 #define MOE_DEC_LDS_MIN_T 1
 #endif
-static size_t lds_rows_bytes(int T, int K) {
-  return T < MOE_DEC_LDS_MIN_T ? (size_t)-1 : (size_t)(T < 16 ? T : 16) * ((size_t)K * 2 + 16);
+static int lds_rows_for(int T, int K) {
+  if (T < MOE_DEC_LDS_MIN_T) return 0;
+  const int fit = (int)(MOE_DEC_LDS_ROWS_MAX / ((size_t)K * 2 + 16));
+  const int want = T < 16 ? T : 16;
+  return fit < want ? fit : want;
 }
 
 template <int WT, int KW, int R>
-static void gu_nt(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int rt) {
-  const size_t lb = lds_rows_bytes(a.T, a.H);
+static void gu_nt(const FfnArgs& a0, hipStream_t st, unsigned grid, int sh, int rt) {
+  FfnArgs a = a0;
+  a.lds_rows = WT == W_MXFP4 && KW == 1 ? lds_rows_for(a.T, a.H) : 0;
+  const size_t lb = (size_t)a.lds_rows * ((size_t)a.H * 2 + 16);
   switch (pick_nt(a.T, WT)) {
     case 1:
-      if (WT == W_MXFP4 && KW == 1 && lb <= MOE_DEC_LDS_ROWS_MAX)
+      if (a.lds_rows > 0)
         launch_ffn_kernel_lds(gate_up_mfma<WT, 1, KW, R, WT == W_MXFP4 && KW == 1>, grid, lb, st, a, sh, rt);
       else
         launch_ffn_kernel(gate_up_mfma<WT, 1, KW, R>, grid, st, a, sh, rt);
@@ -683,11 +716,14 @@ static void gu_nt(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int r
   }
 }
 template <int WT, int KW, int R>
-static void dn_nt(const FfnArgs& a, hipStream_t st, unsigned grid, int sh, int rt) {
-  const size_t lb = lds_rows_bytes(a.T, a.I > a.I_shared ? a.I : a.I_shared);
+static void dn_nt(const FfnArgs& a0, hipStream_t st, unsigned grid, int sh, int rt) {
+  FfnArgs a = a0;
+  const int kmax = a.I > a.I_shared ? a.I : a.I_shared;
+  a.lds_rows = WT == W_MXFP4 && KW == 1 ? lds_rows_for(a.T, kmax) : 0;
+  const size_t lb = (size_t)a.lds_rows * ((size_t)kmax * 2 + 16);
   switch (pick_nt(a.T, WT)) {
     case 1:
-      if (WT == W_MXFP4 && KW == 1 && lb <= MOE_DEC_LDS_ROWS_MAX)
+      if (a.lds_rows > 0)
         launch_ffn_kernel_lds(down_mfma<WT, 1, KW, R, WT == W_MXFP4 && KW == 1>, grid, lb, st, a, sh, rt);
       else
         launch_ffn_kernel(down_mfma<WT, 1, KW, R>, grid, st, a, sh, rt);
@@ -739,7 +775,7 @@ hipError_t launch_ffn_down(int wtype, const FfnArgs& a, hipStream_t st) {
   const int shared_tiles = sh ? tiles : 0;
   const unsigned grid = shared_tiles + a.routed_items * tiles;
   if (!grid) return hipSuccess;
-  if (wtype == W_BF16) dn_nt<W_BF16, 1, 2>(a, st, grid, shared_tiles, tiles);
+  if (wtype == W_BF16) dn_nt<W_BF16, MOE_DEC_BF16_DN_KW, MOE_DEC_BF16_DN_R>(a, st, grid, shared_tiles, tiles);
   else if (sp.r == 1) dn_nt<W_MXFP4, 1, 1>(a, st, grid, shared_tiles, tiles);
   else if (sp.r == 2) dn_nt<W_MXFP4, 1, 2>(a, st, grid, shared_tiles, tiles);
   else dn_nt<W_MXFP4, 1, 4>(a, st, grid, shared_tiles, tiles);

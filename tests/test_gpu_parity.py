@@ -171,6 +171,9 @@ SMALL = [
     (synth.MXFP4, 40, 2048, 2048, 2, 2, False),
     # token rows staged in LDS with K not a multiple of 128 (clamped columns), shared expert
     (synth.MXFP4, 5, 160, 96, 8, 2, True),
+    # H = 4096: the launch's LDS holds 5 token rows, so experts with more tokens (and
+    # the shared expert) read theirs from memory in the same launch
+    (synth.MXFP4, 12, 4096, 256, 4, 2, True),
 ]
 
 
