@@ -39,9 +39,25 @@ template <typename K, typename... Args>
 static void launch_ffn_kernel(K kernel, unsigned grid, hipStream_t st, Args... args) {
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, args...);
 }
-template <typename K, typename... Args>
-static void launch_ffn_kernel_lds(K kernel, unsigned grid, size_t lds, hipStream_t st, Args... args) {
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, st, args...);
+// Waves per block of the MFMA decode kernels: bf16 splits K over up to 4 waves of a
+// block; MXFP4 (no K split) uses 4 with one token tile (the block stages the
+// tokens once for 4 waves) and MOE_DEC_MXN_WPB with more (smaller blocks even out
+// the work per CU: one-wave blocks measured 14% faster at 64 tokens).
+#ifndef MOE_DEC_MX1_WPB
+#define MOE_DEC_MX1_WPB 4
+#endif
+#ifndef MOE_DEC_MXN_WPB
+#define MOE_DEC_MXN_WPB 1
+#endif
+template <int WT, int NT>
+constexpr int dec_wpb() { return WT == W_MXFP4 ? (NT == 1 ? MOE_DEC_MX1_WPB : MOE_DEC_MXN_WPB) : 4; }
+static int dec_wpb_of(int wtype, int nt) {
+  return wtype == W_MXFP4 ? (nt == 1 ? MOE_DEC_MX1_WPB : MOE_DEC_MXN_WPB) : 4;
+}
+
+template <int WT, int NT, typename K, typename... Args>
+static void launch_dec_kernel(K kernel, unsigned grid, size_t lds, hipStream_t st, Args... args) {
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * dec_wpb<WT, NT>()), lds, st, args...);
 }
 
 // ===========================================================================
@@ -405,12 +421,13 @@ __device__ __forceinline__ void stage_rows(uint8_t* lds, const uint16_t* src, in
 // 16-row A tile = gate rows j..j+7 stacked on up rows j..j+7, so the epilogue
 // pairs lane l (gate) with lane l+32 (up) and writes h = SiLU(gate) * up as bf16.
 template <int WT, int NT, int KW, int R, bool LB = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT, NT, LB>::waves))) void gate_up_mfma(
+__global__ __launch_bounds__((64 * dec_wpb<WT, NT>())) __attribute__((amdgpu_waves_per_eu(DecTune<WT, NT, LB>::waves))) void gate_up_mfma(
     FfnArgs a, int shared_tiles, int routed_tiles) {
-  constexpr int RT = 4 / KW;
+  constexpr int RT = dec_wpb<WT, NT>() / KW;
+  static_assert(RT >= 1, "waves per block split by KW");
   const Item it = resolve_item(a, shared_tiles, routed_tiles);
   if (!it.valid) return;
-  __shared__ f32x4 red[KW > 1 ? 4 : 1][R][NT][64];
+  __shared__ f32x4 red[KW > 1 ? dec_wpb<WT, NT>() : 1][R][NT][64];
   const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
   const int rg = wv / KW, kp = wv % KW;
   const int r = lane & 15, g = lane >> 4;
@@ -526,12 +543,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT,
 
 // down: row tile t of a wave is 16 output columns (rows of W2) of one item.
 template <int WT, int NT, int KW, int R, bool LB = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecTune<WT, NT, LB>::waves))) void down_mfma(
+__global__ __launch_bounds__((64 * dec_wpb<WT, NT>())) __attribute__((amdgpu_waves_per_eu(DecTune<WT, NT, LB>::waves))) void down_mfma(
     FfnArgs a, int shared_tiles, int routed_tiles) {
-  constexpr int RT = 4 / KW;
+  constexpr int RT = dec_wpb<WT, NT>() / KW;
+  static_assert(RT >= 1, "waves per block split by KW");
   const Item it = resolve_item(a, shared_tiles, routed_tiles);
   if (!it.valid) return;
-  __shared__ f32x4 red[KW > 1 ? 4 : 1][R][NT][64];
+  __shared__ f32x4 red[KW > 1 ? dec_wpb<WT, NT>() : 1][R][NT][64];
   const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
   const int rg = wv / KW, kp = wv % KW;
   const int r = lane & 15, g = lane >> 4;
@@ -706,13 +724,13 @@ static void gu_nt(const FfnArgs& a0, hipStream_t st, unsigned grid, int sh, int 
   switch (pick_nt(a.T, WT)) {
     case 1:
       if (a.lds_rows > 0)
-        launch_ffn_kernel_lds(gate_up_mfma<WT, 1, KW, R, WT == W_MXFP4 && KW == 1>, grid, lb, st, a, sh, rt);
+        launch_dec_kernel<WT, 1>(gate_up_mfma<WT, 1, KW, R, WT == W_MXFP4 && KW == 1>, grid, lb, st, a, sh, rt);
       else
-        launch_ffn_kernel(gate_up_mfma<WT, 1, KW, R>, grid, st, a, sh, rt);
+        launch_dec_kernel<WT, 1>(gate_up_mfma<WT, 1, KW, R>, grid, 0, st, a, sh, rt);
       break;
-    case 2: launch_ffn_kernel(gate_up_mfma<WT, 2, KW, R>, grid, st, a, sh, rt); break;
-    case 4: launch_ffn_kernel(gate_up_mfma<WT, 4, KW, R>, grid, st, a, sh, rt); break;
-    default: launch_ffn_kernel(gate_up_mfma<WT, 8, KW, R>, grid, st, a, sh, rt); break;
+    case 2: launch_dec_kernel<WT, 2>(gate_up_mfma<WT, 2, KW, R>, grid, 0, st, a, sh, rt); break;
+    case 4: launch_dec_kernel<WT, 4>(gate_up_mfma<WT, 4, KW, R>, grid, 0, st, a, sh, rt); break;
+    default: launch_dec_kernel<WT, 8>(gate_up_mfma<WT, 8, KW, R>, grid, 0, st, a, sh, rt); break;
   }
 }
 template <int WT, int KW, int R>
@@ -724,13 +742,13 @@ static void dn_nt(const FfnArgs& a0, hipStream_t st, unsigned grid, int sh, int 
   switch (pick_nt(a.T, WT)) {
     case 1:
       if (a.lds_rows > 0)
-        launch_ffn_kernel_lds(down_mfma<WT, 1, KW, R, WT == W_MXFP4 && KW == 1>, grid, lb, st, a, sh, rt);
+        launch_dec_kernel<WT, 1>(down_mfma<WT, 1, KW, R, WT == W_MXFP4 && KW == 1>, grid, lb, st, a, sh, rt);
       else
-        launch_ffn_kernel(down_mfma<WT, 1, KW, R>, grid, st, a, sh, rt);
+        launch_dec_kernel<WT, 1>(down_mfma<WT, 1, KW, R>, grid, 0, st, a, sh, rt);
       break;
-    case 2: launch_ffn_kernel(down_mfma<WT, 2, KW, R>, grid, st, a, sh, rt); break;
-    case 4: launch_ffn_kernel(down_mfma<WT, 4, KW, R>, grid, st, a, sh, rt); break;
-    default: launch_ffn_kernel(down_mfma<WT, 8, KW, R>, grid, st, a, sh, rt); break;
+    case 2: launch_dec_kernel<WT, 2>(down_mfma<WT, 2, KW, R>, grid, 0, st, a, sh, rt); break;
+    case 4: launch_dec_kernel<WT, 4>(down_mfma<WT, 4, KW, R>, grid, 0, st, a, sh, rt); break;
+    default: launch_dec_kernel<WT, 8>(down_mfma<WT, 8, KW, R>, grid, 0, st, a, sh, rt); break;
   }
 }
 
@@ -744,7 +762,7 @@ hipError_t launch_ffn_gate_up(int wtype, const FfnArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   const Shape sp = gate_up_shape(wtype, a.T);
-  const int rb = 8 * sp.r * (4 / sp.kw);  // intermediate indices per block
+  const int rb = 8 * sp.r * (dec_wpb_of(wtype, pick_nt(a.T, wtype)) / sp.kw);  // intermediate indices per block
   const int shared_tiles = sh ? (a.I_shared + rb - 1) / rb : 0, routed_tiles = (a.I + rb - 1) / rb;
   const unsigned grid = shared_tiles + a.routed_items * routed_tiles;
   if (!grid) return hipSuccess;
@@ -770,7 +788,7 @@ hipError_t launch_ffn_down(int wtype, const FfnArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   const Shape sp = down_shape(wtype, a.T);
-  const int rb = 16 * sp.r * (4 / sp.kw);  // output columns per block
+  const int rb = 16 * sp.r * (dec_wpb_of(wtype, pick_nt(a.T, wtype)) / sp.kw);  // output columns per block
   const int tiles = (a.H + rb - 1) / rb;
   const int shared_tiles = sh ? tiles : 0;
   const unsigned grid = shared_tiles + a.routed_items * tiles;
