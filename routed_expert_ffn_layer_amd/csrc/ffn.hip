@@ -12,9 +12,12 @@
 // (if any) followed by up to min(E, T*k) routed experts; a block finds "its"
 // routed expert as the a-th expert with pairs and a slot (a scan over offsets in
 // L2), so the grid is sized from T alone and needs no host synchronisation.
-// Weights are streamed from HBM exactly once per expert (per 16*NT tokens);
-// the 4 waves of a block split the reduction dimension K and add their partial
-// accumulators in a fixed order, so results are deterministic run to run.
+// Weights are streamed from HBM exactly once per expert (per 16*NT tokens).
+// The KW waves of a K split add their partial accumulators in a fixed order, so
+// results are deterministic run to run.  Block shapes (waves, K split, row tiles
+// per wave, token tiles per pass) are chosen per weight type and batch by the
+// launchers below; MXFP4 passes of one token tile may first copy their token rows
+// into LDS, and then stream weights through a ring of column steps.
 //
 // MFMA mapping (v_mfma_f32_16x16x32_bf16): weights are the A operand (16 rows),
 // tokens the B operand (16 columns), so a single token costs one weight pass.
