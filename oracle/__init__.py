@@ -62,6 +62,8 @@ def lib():
         L.ora_lru_step.argtypes = [P, i, P, P, P, P, P, P, P, P]
         L.ora_lru_state.restype = None
         L.ora_lru_state.argtypes = [P, P, P]
+        L.ora_lru_resize.restype = i
+        L.ora_lru_resize.argtypes = [P, i, P]
         _lib = L
     return _lib
 
@@ -214,3 +216,12 @@ class LRU:
         ticks = np.empty(self.S, np.int64)
         lib().ora_lru_state(self._h, _p(keys), _p(ticks))
         return keys, ticks
+
+    def resize(self, new_S):
+        """Elastic resize; returns moved_from [new_S] (old slot per new slot, -1 empty)."""
+        moved = np.empty(new_S, np.int32)
+        rc = lib().ora_lru_resize(self._h, new_S, _p(moved))
+        if rc != 0:
+            raise OracleError(f"ora_lru_resize failed with {rc}")
+        self.S = new_S
+        return moved

@@ -445,3 +445,35 @@ void ora_lru_state(const ora_lru* c, int64_t* key_of_slot, int64_t* tick_of_slot
     tick_of_slot[s] = c->tick_of_slot[s];
   }
 }
+
+/* Elastic resize (the pages: the slot pool grows and shrinks with the memory the
+ * GPU can spare, "Three mechanisms", elastic memory management).  Readings: the
+ * resize happens between steps; the kept keys are the most recently used ones and
+ * move to the front of the new pool, most recent first; ticks and the clock carry
+ * over.  Written as a plain selection: repeatedly take the resident key with the
+ * largest tick not yet taken. */
+int ora_lru_resize(ora_lru* c, int new_S, int32_t* moved_from) {
+  if (!c || new_S <= 0 || !moved_from) return -1;
+  int64_t* key2 = (int64_t*)malloc(sizeof(int64_t) * (size_t)new_S);
+  int64_t* tick2 = (int64_t*)malloc(sizeof(int64_t) * (size_t)new_S);
+  char* taken = (char*)calloc((size_t)c->S, 1);
+  if (!key2 || !tick2 || !taken) { free(key2); free(tick2); free(taken); return -2; }
+  for (int s = 0; s < new_S; ++s) {
+    int best = -1;
+    for (int q = 0; q < c->S; ++q)
+      if (!taken[q] && c->key_of_slot[q] >= 0 && (best < 0 || c->tick_of_slot[q] > c->tick_of_slot[best])) best = q;
+    if (best < 0) {
+      key2[s] = -1; tick2[s] = -1; moved_from[s] = -1;
+    } else {
+      taken[best] = 1;
+      key2[s] = c->key_of_slot[best]; tick2[s] = c->tick_of_slot[best]; moved_from[s] = best;
+    }
+  }
+  const size_t nk = (size_t)c->L * (size_t)c->E;
+  for (size_t q = 0; q < nk; ++q) c->slot_of_key[q] = -1;
+  for (int s = 0; s < new_S; ++s)
+    if (key2[s] >= 0) c->slot_of_key[key2[s]] = s;
+  free(c->key_of_slot); free(c->tick_of_slot); free(taken);
+  c->key_of_slot = key2; c->tick_of_slot = tick2; c->S = new_S;
+  return 0;
+}

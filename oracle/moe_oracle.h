@@ -79,6 +79,11 @@ int ora_lru_step(ora_lru* c, int layer, const int32_t* counts, int* n_access, in
                  int64_t* acc_evicted);
 /* key_of_slot [S] (layer*E + expert, -1 if empty) and last-use tick per slot. */
 void ora_lru_state(const ora_lru* c, int64_t* key_of_slot, int64_t* tick_of_slot);
+/* Elastic resize to new_S slots between steps: keeps the min(new_S, resident)
+ * most recently used keys, in new slots 0, 1, ... by decreasing recency, with
+ * their ticks; the others are dropped.  moved_from [new_S] receives the old slot
+ * of each new slot's key (-1 for an empty slot).  Returns 0, or a negative error. */
+int ora_lru_resize(ora_lru* c, int new_S, int32_t* moved_from);
 
 #ifdef __cplusplus
 }

@@ -51,6 +51,17 @@ class BruteLRU:
         return recs
 
 
+def brute_resize(b, new_S):
+    """Truncation written out: keep the new_S most recently used keys, most recent
+    in slot 0; return the old slot of each new slot (-1 empty)."""
+    kept = b.order[::-1][:new_S]                 # most recent first
+    moved = [b.slot[k] for k in kept] + [-1] * (new_S - len(kept))
+    b.order = [k for k in b.order if k in set(kept)]
+    b.slot = {k: s for s, k in enumerate(kept)}
+    b.S = new_S
+    return moved
+
+
 def _counts_from_ids(ids, E):
     return np.bincount(np.asarray(ids).ravel(), minlength=E).astype(np.int32)
 
@@ -209,3 +220,44 @@ def test_workload_shape_against_pages():
     assert routed < fig["total_params_billion"]["value"] * 1e9
     active_routed = c["layers"] * c["k"] * 3 * c["H"] * c["I"]
     assert active_routed < fig["active_params_billion"]["value"] * 1e9
+
+
+def test_lru_resize_matches_brute_force_truncation(ora):
+    """Elastic resize between steps (shrink, grow, down to one slot, beyond the key
+    count): the oracle keeps the most recent keys, most recent first, and later
+    steps go on exactly as the brute-force LRU after the same truncation."""
+    g = np.random.default_rng(5)
+    E, L = 12, 3
+    o = ora.LRU(20, L, E)
+    b = BruteLRU(20)
+    schedule = {40: 7, 80: 30, 120: 1, 140: 16, 200: 50}
+    for t in range(260):
+        if t in schedule:
+            moved = o.resize(schedule[t])
+            assert list(moved) == brute_resize(b, schedule[t])
+        layer = int(g.integers(L))
+        ids = np.stack([g.choice(E, size=3, replace=False) for _ in range(int(g.integers(1, 4)))])
+        counts = _counts_from_ids(ids, E)
+        r = o.step(layer, counts)
+        recs = b.step(layer, E, counts)
+        got = list(zip(r["expert"], r["hit"], r["slot"], r["wave"], r["cold"], r["evicted"]))
+        assert [tuple(int(v) for v in x) for x in got] == recs, t
+    keys, ticks = o.state()
+    assert {int(k): s for s, k in enumerate(keys) if k >= 0} == b.slot
+    assert [int(keys[s]) for s in np.argsort(ticks) if keys[s] >= 0] == b.order
+
+
+def test_lru_resize_closed_forms(ora):
+    E = 8
+    o = ora.LRU(6, 1, E)
+    o.step(0, np.array([1, 1, 1, 1, 0, 0, 0, 0], np.int32))   # keys 0..3 in slots 0..3
+    o.step(0, np.array([0, 0, 1, 0, 0, 0, 0, 0], np.int32))   # key 2 most recent
+    keys_before, _ = o.state()
+    moved = o.resize(1)                                       # only the most recent survives
+    assert list(moved) == [int(np.where(keys_before == 2)[0][0])]
+    keys, _ = o.state()
+    assert list(keys) == [2]
+    moved = o.resize(4)                                       # growing keeps everything
+    assert list(moved) == [0, -1, -1, -1]
+    r = o.step(0, np.array([0, 0, 1, 1, 0, 0, 0, 0], np.int32))
+    assert list(r["hit"]) == [1, 0] and list(r["slot"]) == [0, 1]
