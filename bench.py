@@ -777,7 +777,21 @@ def workload_cached_trace_bf16(args):
     t0 = time.perf_counter()
     tot = run(cache, tokens)
     el = time.perf_counter() - t0
+    # elastic resize of the warm cache to half its slots (kept experts move device to device)
+    half = S // 2
+    new_pool = torch.empty((half, stride), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    moved = cache.resize(half, new_pool, stride)
+    torch.cuda.synchronize()
+    t_resize = time.perf_counter() - t1
+    kept = int((moved >= 0).sum())
+    resize = {"from_slots": S, "to_slots": half, "kept": kept, "ms": t_resize * 1e3,
+              "moved_gbs": kept * eb / t_resize / 1e9,
+              "hbm_frac": 2 * kept * eb / t_resize / 1e9 / HBM_PEAK_GBS}
+    progress(f"cached trace: resize {S} -> {half} slots in {t_resize * 1e3:.1f} ms")
     cache.close()
+    del new_pool
     progress(f"cached trace: {tokens} tokens in {el:.1f} s, miss rate {tot['misses'] / max(tot['accesses'], 1):.3f}")
     bp = host_to_device_gbs(eb)
     fill_gbs = tot["fill_bytes"] / el / 1e9
@@ -798,7 +812,8 @@ def workload_cached_trace_bf16(args):
         cache={"accesses": tot["accesses"], "hits": tot["hits"], "misses": tot["misses"],
                "miss_rate": tot["misses"] / max(tot["accesses"], 1), "fill_bytes": tot["fill_bytes"],
                "fill_gbs": fill_gbs, "host_to_device_gbs_one_expert": bp, "waves": tot["waves"],
-               "expert_read_gbs": tot["accesses"] * eb / el / 1e9})
+               "expert_read_gbs": tot["accesses"] * eb / el / 1e9},
+        resize=resize)
 
 
 def cpu_cached_trace(trace, host, c, n_layers, n_host, S, seconds):

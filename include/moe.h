@@ -189,6 +189,21 @@ int moe_cache_lookup_fill(moe_cache* c, int layer, const int32_t* counts, int wa
  * must be 16-byte aligned and distinct. */
 int moe_cache_lookup_fill_split(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_hits,
                                 int32_t* slot_misses, moe_cache_stats* stats_host, hipStream_t compute_stream);
+/* Elastic resize of the slot pool (the pages: the expert pool grows and shrinks
+ * with the memory the GPU can spare, "Three mechanisms", elastic memory
+ * management).  Between steps only (MOE_ESTATE while a step's waves are open):
+ * keeps the min(n_slots, resident) most recently used keys, most recent first in
+ * new slots 0, 1, ..., with their recency; the others are dropped (later accesses
+ * miss).  Nothing is read from the host pool.  Device handle: slot_pool is the new
+ * pool (n_slots * slot_stride bytes, stride >= expert_bytes and a multiple of 256,
+ * not overlapping the current pool); in-flight fills are waited for, then each
+ * kept expert is copied from its old slot on `stream` (after the work already on
+ * it); the caller may free the old pool once that work is done.  Host-only handle:
+ * slot_pool must be NULL.  moved_from_host (nullable, [n_slots]) receives the old
+ * slot of each new slot's expert, -1 for an empty slot.  On error the cache is
+ * unchanged. */
+int moe_cache_resize(moe_cache* c, int n_slots, void* slot_pool, size_t slot_stride, int32_t* moved_from_host,
+                     hipStream_t stream);
 /* Makes compute_stream wait for the fills of the last split lookup (no-op if it
  * had none or they were already waited for).  A later lookup on the handle
  * inserts this wait itself if the caller skipped it. */

@@ -548,6 +548,56 @@ int moe_cache_lookup_fill_split(moe_cache* c, int layer, const int32_t* counts, 
                             "moe_cache_lookup_fill_split");
 }
 
+int moe_cache_resize(moe_cache* c, int n_slots, void* slot_pool, size_t slot_stride, int32_t* moved_from_host,
+                     hipStream_t stream) {
+  if (!c) return fail(MOE_EINVAL, "null cache");
+  if (n_slots < 1) return fail(MOE_EINVAL, "moe_cache_resize: n_slots=%d must be >= 1", n_slots);
+  if (c->core.step_open()) return fail(MOE_ESTATE, "moe_cache_resize: a step is still open (finish its waves first)");
+  std::vector<int32_t> moved;
+  c->core.plan_resize(n_slots, moved);
+  if (c->device) {
+    if (!slot_pool || !aligned16(slot_pool)) return fail(MOE_EINVAL, "moe_cache_resize: slot_pool must be a 16-byte aligned device pointer");
+    if (slot_stride < c->desc.expert_bytes || slot_stride % 256)
+      return fail(MOE_EINVAL, "moe_cache_resize: slot_stride must be >= expert_bytes and a multiple of 256");
+    const uintptr_t a0 = (uintptr_t)slot_pool, a1 = a0 + (uintptr_t)n_slots * slot_stride;
+    const uintptr_t b0 = (uintptr_t)c->desc.slot_pool, b1 = b0 + (uintptr_t)c->desc.n_slots * c->desc.slot_stride;
+    if (a0 < b1 && b0 < a1) return fail(MOE_EINVAL, "moe_cache_resize: the new slot pool overlaps the current one");
+    // in-flight fills write the current pool: let them land first
+    hipError_t e = hipEventSynchronize(c->ev_fill);
+    if (e != hipSuccess) return hip_fail(e, "moe_cache_resize: waiting for fills");
+    c->fill_pending = false;
+    // kept experts move device to device, after the work already on `stream`
+    std::vector<int32_t> from, to;
+    for (int q = 0; q < n_slots; ++q)
+      if (moved[q] >= 0) {
+        from.push_back(moved[q]);
+        to.push_back(q);
+      }
+    if (c->desc.expert_bytes % 16 == 0 && aligned16(c->desc.slot_pool)) {
+      e = moe::launch_move_slots(static_cast<const uint8_t*>(c->desc.slot_pool), c->desc.slot_stride,
+                                 static_cast<uint8_t*>(slot_pool), slot_stride, c->desc.expert_bytes, from.data(),
+                                 to.data(), (int)from.size(), stream);
+      if (e != hipSuccess) return hip_fail(e, "moe_cache_resize: moving experts");
+    } else {
+      for (size_t q = 0; q < from.size(); ++q) {
+        e = hipMemcpyAsync(static_cast<uint8_t*>(slot_pool) + (size_t)to[q] * slot_stride,
+                           static_cast<const uint8_t*>(c->desc.slot_pool) + (size_t)from[q] * c->desc.slot_stride,
+                           c->desc.expert_bytes, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "moe_cache_resize: moving an expert");
+      }
+    }
+    c->desc.slot_pool = slot_pool;
+    c->desc.slot_stride = slot_stride;
+  } else if (slot_pool) {
+    return fail(MOE_EINVAL, "moe_cache_resize: a host-only handle takes no slot_pool");
+  }
+  c->core.commit_resize(n_slots, moved);
+  c->desc.n_slots = n_slots;
+  if (moved_from_host)
+    for (int q = 0; q < n_slots; ++q) moved_from_host[q] = moved[q];
+  return MOE_OK;
+}
+
 int moe_cache_wait_fills(moe_cache* c, hipStream_t compute_stream) {
   if (!c) return fail(MOE_EINVAL, "null cache");
   if (!c->device) return fail(MOE_EINVAL, "moe_cache_wait_fills needs a device cache (slot_pool set)");

@@ -143,4 +143,38 @@ void LruCore::state(int64_t* key_of_slot, int64_t* tick_of_slot) const {
   }
 }
 
+void LruCore::plan_resize(int new_S, std::vector<int32_t>& moved_from) const {
+  std::vector<int32_t> resident;
+  for (int q = 0; q < S_; ++q)
+    if (key_of_slot_[q] >= 0) resident.push_back(q);
+  std::sort(resident.begin(), resident.end(),
+            [&](int32_t x, int32_t y) { return tick_of_slot_[x] > tick_of_slot_[y]; });
+  moved_from.assign(new_S, -1);
+  const int keep = (int)std::min<size_t>((size_t)new_S, resident.size());
+  for (int q = 0; q < keep; ++q) moved_from[q] = resident[q];
+}
+
+void LruCore::commit_resize(int new_S, const std::vector<int32_t>& moved_from) {
+  std::vector<int64_t> key2(new_S, -1), tick2(new_S, -1);
+  for (int q = 0; q < S_; ++q)
+    if (key_of_slot_[q] >= 0) slot_of_key_[key_of_slot_[q]] = -1;
+  int keep = 0;
+  for (int q = 0; q < new_S; ++q) {
+    if (moved_from[q] < 0) continue;
+    key2[q] = key_of_slot_[moved_from[q]];
+    tick2[q] = tick_of_slot_[moved_from[q]];
+    slot_of_key_[key2[q]] = q;
+    keep = q + 1;
+  }
+  S_ = new_S;
+  key_of_slot_.swap(key2);
+  tick_of_slot_.swap(tick2);
+  prev_.assign(new_S, -1);
+  next_.assign(new_S, -1);
+  head_ = tail_ = -1;
+  for (int q = keep - 1; q >= 0; --q) push_tail(q);  // least recent (highest slot) first
+  free_.clear();
+  for (int q = keep; q < new_S; ++q) free_.insert(q);
+}
+
 }  // namespace moe

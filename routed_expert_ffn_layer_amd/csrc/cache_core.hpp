@@ -66,6 +66,12 @@ class LruCore {
   // Snapshot for comparison: key per slot (-1 empty) and last-use tick.
   void state(int64_t* key_of_slot, int64_t* tick_of_slot) const;
 
+  // Elastic resize between steps: keep the min(new_S, resident) most recently used
+  // keys, most recent first in new slots 0, 1, ...; moved_from[s] is the old slot
+  // of new slot s (-1 empty).  plan_resize does not change the cache.
+  void plan_resize(int new_S, std::vector<int32_t>& moved_from) const;
+  void commit_resize(int new_S, const std::vector<int32_t>& moved_from);
+
  private:
   void unlink(int s);
   void push_tail(int s);

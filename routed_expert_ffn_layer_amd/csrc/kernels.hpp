@@ -18,6 +18,13 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* coun
 hipError_t launch_combine(const float* rows, const float* w, const int32_t* inv, const float* shared, int T, int k,
                           int H, void* y, bool bf16_out, hipStream_t st);
 
+// Elastic cache resize: copy `bytes` of each of n experts from slot from[i] of
+// one pool to slot to[i] of another (batched launches, the table in the kernel
+// arguments).  Expert bytes must be a multiple of 16 and the pools 16-byte aligned.
+constexpr int kMoveBatch = 480;
+hipError_t launch_move_slots(const uint8_t* src, uint64_t src_stride, uint8_t* dst, uint64_t dst_stride,
+                             uint64_t bytes, const int32_t* from, const int32_t* to, int n, hipStream_t st);
+
 // Grouped FFN phases.  wtype: 0 f32, 1 bf16, 2 mxfp4.
 hipError_t launch_ffn_gate_up(int wtype, const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_down(int wtype, const FfnArgs& a, hipStream_t st);

@@ -53,7 +53,7 @@ class LayerStreamDesc(ctypes.Structure):
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_last_error", "moe_expert_bytes", "moe_route_topk",
            "moe_permute", "moe_cache_create", "moe_cache_destroy", "moe_cache_lookup_fill",
            "moe_cache_lookup_host", "moe_cache_state", "moe_cache_inject_fill_failure",
-           "moe_cache_lookup_fill_split", "moe_cache_wait_fills", "moe_route",
+           "moe_cache_lookup_fill_split", "moe_cache_wait_fills", "moe_route", "moe_cache_resize",
            "moe_grouped_ffn_workspace", "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down",
            "moe_combine", "moe_layer_stream_create", "moe_layer_stream_destroy", "moe_layer_stream_fill",
            "moe_layer_stream_acquire", "moe_layer_stream_release"]
@@ -83,6 +83,7 @@ def lib():
     L.moe_cache_lookup_host.argtypes = [P, i, P, i, P, P, i, ctypes.POINTER(i), ctypes.POINTER(CacheStats)]
     L.moe_cache_lookup_fill_split.argtypes = [P, i, P, i, P, P, ctypes.POINTER(CacheStats), P]
     L.moe_cache_wait_fills.argtypes = [P, P]
+    L.moe_cache_resize.argtypes = [P, i, P, sz, P, P]
     L.moe_cache_state.argtypes = [P, P, P]
     L.moe_cache_inject_fill_failure.argtypes = [P, ctypes.c_int64]
     L.moe_grouped_ffn_workspace.restype = sz
@@ -218,6 +219,18 @@ class MoeCache:
         _check(lib().moe_cache_lookup_fill_split(self._h, layer, _ptr(counts), wave, _ptr(slot_hits),
                                                  _ptr(slot_misses), ctypes.byref(st), _stream(stream)))
         return st.as_dict()
+
+    def resize(self, n_slots, slot_pool=None, slot_stride=0, stream=None):
+        """Elastic resize; returns moved_from (numpy int32 [n_slots]).  The handle keeps
+        the new pool alive; the old one may be released once `stream` has run the copies."""
+        import numpy as np
+        moved = np.empty(n_slots, np.int32)
+        st = ctypes.c_void_p(0) if slot_pool is None and stream is None else _stream(stream)
+        _check(lib().moe_cache_resize(self._h, n_slots, _ptr(slot_pool), slot_stride,
+                                      moved.ctypes.data_as(ctypes.c_void_p), st))
+        self.n_slots = n_slots
+        self._keep = (slot_pool,) + tuple(self._keep[1:])
+        return moved
 
     def wait_fills(self, stream=None):
         _check(lib().moe_cache_wait_fills(self._h, _stream(stream)))

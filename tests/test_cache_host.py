@@ -119,3 +119,34 @@ def test_injected_fill_failure_invalidates_touched_slots_only(ora):
     table, fills, st = c.lookup_host(0, counts, 0)
     assert all(table[e] >= 0 for e in (1, 2, 3, 4, 5))
     assert len(set(table[[1, 2, 3, 4, 5]])) == 5
+
+
+def test_resize_between_steps_matches_oracle(ora):
+    """Elastic resize of a host-only handle: same kept keys, slots and moves as the
+    oracle; later steps identical; resizing inside an open step is refused."""
+    g = np.random.default_rng(11)
+    E, L, S = 16, 3, 12
+    c = moe.MoeCache(L, E, S)
+    o = ora.LRU(S, L, E)
+    for t, new_S in ((60, 5), (120, 30), (150, 1), (170, 9)):
+        while True:
+            layer = int(g.integers(0, L))
+            ids = g.choice(E, size=int(g.integers(1, 7)), replace=False)
+            _step_both(c, o, layer, _counts(ids, E), E, c.n_slots)
+            t -= 1
+            if t <= 0:
+                break
+        np.testing.assert_array_equal(c.resize(new_S), o.resize(new_S))
+        _same_state(c, o)
+    for _ in range(50):
+        layer = int(g.integers(0, L))
+        _step_both(c, o, layer, _counts(g.choice(E, size=4, replace=False), E), E, c.n_slots)
+    _same_state(c, o)
+    # a step with two waves left open: resize refused, the cache untouched
+    c2 = moe.MoeCache(1, E, 2)
+    c2.lookup_host(0, _counts(np.arange(5), E), 0)
+    with pytest.raises(moe.MoeError) as e:
+        c2.resize(4)
+    assert e.value.status == moe.MOE_ESTATE
+    with pytest.raises(moe.MoeError):
+        c.resize(0)

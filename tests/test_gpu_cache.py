@@ -177,3 +177,47 @@ def test_device_fill_failure_keeps_cache_consistent(ora):
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
     cache.close()
+
+
+def test_device_resize_mid_trace(ora):
+    """Elastic resize of a device cache between steps: shrink to a new pool, later
+    grow to another; the kept experts are copied device to device (never from the
+    host pool), every layer stays bitwise equal to the resident layer and the state
+    equals the oracle's after every step."""
+    H, I, E, k, Ls, tokens = 128, 64, 32, 4, 4, 24
+    seed = 1009
+    lg = synth.trace_logits(seed, tokens, Ls, E, s=1.0, reuse_p=0.7)
+    experts = np.stack([synth.random_expert(synth.BF16, H, I, synth.rng(seed, 3, l, e)) for l in range(Ls)
+                        for e in range(E)])
+    eb = experts.shape[1]
+    host = _pinned_pool(experts)
+    S = 40
+    cache, slot_pool, stride = _device_cache(Ls, E, S, eb, host)
+    lru = ora.LRU(S, Ls, E)
+    resident = to_dev(experts)
+    b = L.LayerBuffers(1, E, k, H, I, synth.BF16)
+    bc = L.LayerBuffers(1, E, k, H, I, synth.BF16)
+    pool = slot_pool
+    for t in range(tokens):
+        if t in (8, 16):
+            new_S = 11 if t == 8 else 60
+            new_pool = torch.zeros((new_S, stride), dtype=torch.uint8, device=dev())
+            log(f"resize to {new_S} at token {t}")
+            moved = cache.resize(new_S, new_pool, stride)
+            np.testing.assert_array_equal(moved, lru.resize(new_S))
+            torch.cuda.synchronize()
+            for s_new, s_old in enumerate(moved):   # the kept experts' bytes moved
+                if s_old >= 0:
+                    assert torch.equal(new_pool[s_new, :eb], pool[s_old, :eb])
+            pool = new_pool
+            _same_state(cache, lru)
+        x = to_dev(synth.encode_activations(synth.BF16, synth.normal_x(seed, 1, H, t)))
+        for l in range(Ls):
+            lg_d = to_dev(lg[t, l][None, :])
+            y_ref = _resident_y(b, lg_d, x, resident[l * E:(l + 1) * E], eb, E)
+            y, waves = L.forward_cached(bc, cache, l, lg_d, x, pool, stride)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), (t, l)
+            lru.step(l, bc.counts.cpu().numpy())
+            _same_state(cache, lru)
+    cache.close()
