@@ -62,6 +62,8 @@ def lib():
         L.ora_lru_step.argtypes = [P, i, P, P, P, P, P, P, P, P]
         L.ora_lru_state.restype = None
         L.ora_lru_state.argtypes = [P, P, P]
+        L.ora_router_logits.restype = i
+        L.ora_router_logits.argtypes = [P, P, i, i, i, P]
         L.ora_lru_resize.restype = i
         L.ora_lru_resize.argtypes = [P, i, P]
         _lib = L
@@ -119,6 +121,17 @@ def route_topk(logits, k):
     w64 = np.empty((T, k), dtype=np.float64)
     _check(lib().ora_route_topk(_p(logits), T, E, k, _p(ids), _p(w32), _p(w64)), "route_topk")
     return ids, w32, w64
+
+
+def router_logits(x_bits, wr_bits):
+    """x [T][H], wr [E][H] bf16 bits (uint16) -> fp64 logits [T][E]."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    wr = np.ascontiguousarray(wr_bits, dtype=np.uint16)
+    T, H = x.shape
+    E = wr.shape[0]
+    out = np.empty((T, E))
+    _check(lib().ora_router_logits(_p(x), _p(wr), T, H, E, _p(out)), "router_logits")
+    return out
 
 
 def permute(ids, E):

@@ -477,3 +477,19 @@ int ora_lru_resize(ora_lru* c, int new_S, int32_t* moved_from) {
   c->key_of_slot = key2; c->tick_of_slot = tick2; c->S = new_S;
   return 0;
 }
+
+/* Router projection (a reading: the pages say the engine leaves the model's router
+ * as it is, "Three mechanisms", bandwidth-adaptive execution, and do not give the
+ * router; the plain linear gate of an MoE layer is used, logits = W_r x).  Each
+ * logit is the exact products of the bf16 values summed in fp64 in h order. */
+int ora_router_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E, double* logits) {
+  if (T < 0 || H <= 0 || E <= 0 || (T > 0 && (!x || !wr || !logits))) return -1;
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int h = 0; h < H; ++h)
+        acc += ora_bf16_value(x[(size_t)t * H + h]) * ora_bf16_value(wr[(size_t)e * H + h]);
+      logits[(size_t)t * E + e] = acc;
+    }
+  return 0;
+}

@@ -41,6 +41,9 @@ int ora_decode_x(int dtype, const void* x, int T, int H, double* out);
  * the k selected logits.  ids [T][k]; w32 (nullable) the weights rounded to f32;
  * w64 (nullable) the weights in fp64.  Rejects non-finite logits (-2). */
 int ora_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w32, double* w64);
+/* Router projection ahead of top-k: logits[t][e] = sum_h x[t][h] * wr[e][h] with x
+ * [T][H] and wr [E][H] bf16 bits, products and sum in fp64 (h ascending). */
+int ora_router_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E, double* logits);
 
 /* Stable counting sort of the T*k (token, choice) pairs r = t*k + j by expert. */
 int ora_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,

@@ -10,6 +10,8 @@ import numpy as np
 import pytest
 from scipy.special import softmax
 
+import synth
+
 
 def _brute_topk(row, k):
     order = sorted(range(len(row)), key=lambda e: (-float(row[e]), e))
@@ -116,3 +118,31 @@ def test_permute_matches_brute_force(ora, T, k, E):
 def test_permute_empty(ora):
     counts, offsets, s, inv = ora.permute(np.zeros((0, 4), np.int32), 16)
     assert counts.sum() == 0 and np.all(offsets == 0) and s.size == 0 and inv.size == 0
+
+
+def test_router_logits_against_float64_matmul(ora):
+    """The router projection equals a float64 matrix product of the decoded bf16
+    inputs (numpy), to fp64 rounding."""
+    g = np.random.default_rng(21)
+    T, H, E = 5, 96, 24
+    x = synth.bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    wr = synth.bf16_bits((g.standard_normal((E, H)) * 0.02).astype(np.float32))
+    got = ora.router_logits(x, wr)
+    ref = synth.bf16_bits_to_f32(x).astype(np.float64) @ synth.bf16_bits_to_f32(wr).astype(np.float64).T
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_router_logits_closed_forms(ora):
+    g = np.random.default_rng(22)
+    H, E = 64, 10
+    wr = synth.bf16_bits((g.standard_normal((E, H)) * 0.02).astype(np.float32))
+    w = synth.bf16_bits_to_f32(wr).astype(np.float64)
+    # a one-hot token picks one column of the router exactly
+    x = np.zeros((1, H), np.float32); x[0, 17] = 1.0
+    np.testing.assert_array_equal(ora.router_logits(synth.bf16_bits(x), wr)[0], w[:, 17])
+    # scaling a token by 2 doubles every logit exactly; the zero token gives zeros
+    xs = synth.bf16_bits(g.standard_normal((3, H)).astype(np.float32))
+    l1 = ora.router_logits(xs, wr)
+    x2 = synth.bf16_bits(2 * synth.bf16_bits_to_f32(xs))
+    np.testing.assert_array_equal(ora.router_logits(x2, wr), 2 * l1)
+    np.testing.assert_array_equal(ora.router_logits(np.zeros((2, H), np.uint16), wr), np.zeros((2, E)))
