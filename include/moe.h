@@ -112,6 +112,18 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, i
 int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w, int32_t* counts,
               int32_t* offsets, int32_t* sorted_rows, int32_t* inv_rows, hipStream_t stream);
 
+/* Router projection then moe_route: logits[t][e] = sum_h x[t][h] * w_router[e][h]
+ * (x [T][H] and w_router [E][H] bf16, f32 accumulation in a fixed order, written
+ * to logits [T][E] f32), then top-k gating and the permutation on those logits
+ * exactly as moe_route.  H a positive multiple of 8.  The pages leave the model's
+ * router as it is ("Three mechanisms", bandwidth-adaptive execution); the plain
+ * linear gate of an MoE layer is computed.  Selections follow the f32 logits, so
+ * they can differ from an exact-arithmetic selection only where two logits are
+ * within the summation error of each other. */
+int moe_route_project(const void* x, const void* w_router, int T, int H, int E, int k, float* logits,
+                      int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_rows,
+                      int32_t* inv_rows, hipStream_t stream);
+
 /* ------------------------------------------------------------------------- */
 /* Expert-slot cache.  The pages: inactive experts sit in host memory and enter
  * the execution path on demand ("The gap it targets"); during decode a shared

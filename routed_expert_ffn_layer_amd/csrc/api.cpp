@@ -140,6 +140,29 @@ int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route launch");
 }
 
+int moe_route_project(const void* x, const void* w_router, int T, int H, int E, int k, float* logits,
+                      int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_rows,
+                      int32_t* inv_rows, hipStream_t stream) {
+  if (int rc = check_routing(T, E, k)) return rc;
+  if (H <= 0 || H % 8) return fail(MOE_EINVAL, "moe_route_project: H=%d must be a positive multiple of 8", H);
+  REQUIRE_PTR(counts);
+  REQUIRE_PTR(offsets);
+  if (T > 0) {
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(w_router);
+    REQUIRE_PTR(logits);
+    REQUIRE_PTR(topk_ids);
+    REQUIRE_PTR(topk_w);
+    REQUIRE_PTR(sorted_rows);
+    REQUIRE_PTR(inv_rows);
+  }
+  hipError_t e = moe::launch_router_logits(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), T,
+                                           H, E, logits, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_route_project projection launch");
+  e = moe::launch_route(logits, T, E, k, topk_ids, topk_w, counts, offsets, sorted_rows, inv_rows, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route_project route launch");
+}
+
 int moe_combine(const float* out_rows, const float* topk_w, const int32_t* inv_rows, const float* shared_out, int T,
                 int k, int H, void* y, int ydt, hipStream_t stream) {
   if (T < 0 || k < 1 || k > 32 || H <= 0 || H % 4) return fail(MOE_EINVAL, "moe_combine: bad T=%d k=%d H=%d", T, k, H);

@@ -10,6 +10,9 @@ namespace moe {
 struct FfnArgs;
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st);
+// Router projection: logits [T][E] = x [T][H] . wr [E][H]^T (bf16 in, f32 out).
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E, float* logits,
+                                hipStream_t st);
 // Top-k then permutation; one workgroup launch for small batches.
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_rows, int32_t* inv_rows, hipStream_t st);

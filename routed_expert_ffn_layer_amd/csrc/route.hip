@@ -85,6 +85,50 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   topk_row<EPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
 }
 
+// ---------------------------------------------------------------------------
+// Router projection ahead of top-k: logits[t][e] = x[t] . Wr[e] (bf16 inputs,
+// f32 accumulation).  A wave computes kRouterEPW experts of one token; lanes stride
+// over H in 16-byte pieces (8 bf16), each piece a run of f32 fused multiply-adds of
+// exact bf16 products, then a fixed butterfly sums the lanes, so the result is the
+// same on every run.  Grid (T, E / (4 * kRouterEPW)) of 4-wave blocks.
+// ---------------------------------------------------------------------------
+constexpr int kRouterEPW = 4;
+
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ wr, int H, int E,
+                                                            float* __restrict__ logits) {
+  const int t = blockIdx.x, lane = threadIdx.x & 63;
+  const int e0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * kRouterEPW;
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
+  const int pieces = H / 8;
+#pragma unroll
+  for (int q = 0; q < kRouterEPW; ++q) {
+    const int e = e0 + q;
+    if (e >= E) break;  // uniform per wave
+    const u32x4* wrow = reinterpret_cast<const u32x4*>(wr + (size_t)e * H);
+    float acc = 0.0f;
+    for (int c = lane; c < pieces; c += 64) {
+      const u32x4 xv = xr[c], wv = wrow[c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = fmaf(__uint_as_float(xv[i] << 16), __uint_as_float(wv[i] << 16), acc);
+        acc = fmaf(__uint_as_float(xv[i] & 0xffff0000u), __uint_as_float(wv[i] & 0xffff0000u), acc);
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, 64);
+    if (lane == 0) logits[(size_t)t * E + e] = acc;
+  }
+}
+
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E, float* logits,
+                                hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((unsigned)T, (unsigned)((E + 4 * kRouterEPW - 1) / (4 * kRouterEPW))), block(256);
+  hipLaunchKernelGGL(router_logits_kernel, grid, block, 0, st, x, wr, H, E, logits);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const dim3 grid((T + 3) / 4), block(256);

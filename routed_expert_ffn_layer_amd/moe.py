@@ -53,7 +53,7 @@ class LayerStreamDesc(ctypes.Structure):
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_last_error", "moe_expert_bytes", "moe_route_topk",
            "moe_permute", "moe_cache_create", "moe_cache_destroy", "moe_cache_lookup_fill",
            "moe_cache_lookup_host", "moe_cache_state", "moe_cache_inject_fill_failure",
-           "moe_cache_lookup_fill_split", "moe_cache_wait_fills", "moe_route", "moe_cache_resize",
+           "moe_cache_lookup_fill_split", "moe_cache_wait_fills", "moe_route", "moe_cache_resize", "moe_route_project",
            "moe_grouped_ffn_workspace", "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down",
            "moe_combine", "moe_layer_stream_create", "moe_layer_stream_destroy", "moe_layer_stream_fill",
            "moe_layer_stream_acquire", "moe_layer_stream_release"]
@@ -77,6 +77,7 @@ def lib():
     L.moe_route_topk.argtypes = [P, i, i, i, P, P, P]
     L.moe_permute.argtypes = [P, i, i, i, P, P, P, P, P]
     L.moe_route.argtypes = [P, i, i, i, P, P, P, P, P, P, P]
+    L.moe_route_project.argtypes = [P, P, i, i, i, i, P, P, P, P, P, P, P, P]
     L.moe_cache_create.argtypes = [ctypes.POINTER(CacheDesc), ctypes.POINTER(P)]
     L.moe_cache_destroy.argtypes = [P]
     L.moe_cache_lookup_fill.argtypes = [P, i, P, i, P, ctypes.POINTER(CacheStats), P]
@@ -137,6 +138,14 @@ def moe_route(logits, k, topk_ids, topk_w, counts, offsets, sorted_rows, inv_row
     T, E = logits.shape
     _check(lib().moe_route(_ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets),
                            _ptr(sorted_rows), _ptr(inv_rows), _stream(stream)))
+
+
+def moe_route_project(x, w_router, k, logits, topk_ids, topk_w, counts, offsets, sorted_rows, inv_rows,
+                      stream=None):
+    T, H = x.shape
+    E = w_router.shape[0]
+    _check(lib().moe_route_project(_ptr(x), _ptr(w_router), T, H, E, k, _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+                                   _ptr(counts), _ptr(offsets), _ptr(sorted_rows), _ptr(inv_rows), _stream(stream)))
 
 
 def moe_permute(topk_ids, E, counts, offsets, sorted_rows, inv_rows, stream=None):
