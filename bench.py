@@ -2,25 +2,31 @@
 """MoE-layer throughput on one MI355X, with the roofline of the dominant kernel
 and the CPU oracle timed beside it.
 
-Default workload (--workload decode_bf16): the bf16 decode layer (hidden 2048,
-256 routed experts plus one always-on shared expert, top-8, expert intermediate
-512) at 16 tokens per layer, stacked as 16 layers with distinct weights (16
-replicas of the 257 experts, 26 GB) so that the 256 MB Infinity Cache cannot
-serve re-used weights.  A step is one pass of the whole path (top-k,
-permutation, grouped FFN gate_up + down, combine) through the 16 layers; every
-layer has its own seeded logits and activations, all resident in HBM before the
-timed region.  All experts are resident (fixed identity slot table).
+Default workload (--workload prefill_mxfp4): 4096-token prefill layers of the
+MXFP4 shape (hidden 4096, 256 routed experts, top-6, expert intermediate 2048,
+E2M1 weights with an E8M0 scale per 32-element block, bf16 activations), N(0,1)
+logits so that every expert is active with about 96 tokens.  A step is one
+4096-token chunk through 43 layers: every layer's 3.42 GB of expert weights come
+from pinned host memory into one of two HBM banks while the previous layer runs
+the whole path (top-k, permutation, grouped GEMM gate_up + down, combine).  The
+line's roofline is the grouped GEMM gate_up kernel against the bf16 MFMA peak.
+The same run then measures the MXFP4 decode stack (43 layers, every expert
+resident, batches of 64, 1 and 8 tokens) and reports it under "decode_mxfp4"
+with its own HBM roofline (--no-decode-leg skips it).
 
 Other workloads, each printing one JSON line of the same form:
-  decode_mxfp4       43 stacked MXFP4 layers (hidden 4096, 256 experts, top-6,
-                     intermediate 2048), all 11,008 experts resident, Zipf(1.1)
-                     popularity + N(0,1) logits, batches 64, 1 and 8.
-  prefill_mxfp4      4096-token layers of that shape; each layer's weights come
-                     from pinned host memory into one of two HBM banks while the
-                     previous layer computes (43 layers).
+  decode_mxfp4       the MXFP4 decode stack alone (headline batch 64).
+  decode_bf16        16 stacked bf16 decode layers (hidden 2048, 256 routed
+                     experts + 1 shared, top-8, intermediate 512), batches 16, 1, 4.
   cached_trace_bf16  1000 single-token steps through 48 bf16 layers with a cold
                      global-LRU slot cache holding 37% of the experts.
   hostbw             pinned host -> HBM copy bandwidth at the fill sizes.
+
+CPU baseline: the oracle (plain fp64 C, test infrastructure) on a bounded
+sample of the same workload, once on one thread and once with its per-expert
+calls spread over every host core allotted to the process (a thread pool over
+experts; each call is the unmodified oracle routine; rows are combined per token
+in a fixed order).
 """
 import argparse
 import ctypes
@@ -53,7 +59,7 @@ WORKLOADS = ("decode_bf16", "decode_mxfp4", "prefill_mxfp4", "cached_trace_bf16"
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=WORKLOADS, default="decode_bf16")
+    ap.add_argument("--workload", choices=WORKLOADS, default="prefill_mxfp4")
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default depends on the workload)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default depends on the workload)")
     ap.add_argument("--tokens", type=int, default=None, help="tokens per layer of the headline batch")
@@ -68,10 +74,17 @@ def parse():
                          "graph per step, replayed)")
     ap.add_argument("--split-waves", action="store_true",
                     help="cached_trace_bf16: compute each wave's hits while its misses fill (default: after all fills)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="budget of each oracle CPU baseline leg (one thread, all cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-leg", action="store_true",
+                    help="prefill_mxfp4: skip the MXFP4 decode stack measured after the prefill line")
+    ap.add_argument("--cpu-threads", type=int, default=None,
+                    help="threads of the all-core CPU baseline (default: the cores allotted to this process)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--summarize-pmc", metavar="PROF_DIR", default=None,
+                    help="print per-kernel averages of every counter in rocprofv3 --pmc runs (no GPU)")
     ap.add_argument("--summarize-counters", metavar="PROF_DIR", default=None,
                     help="print per-kernel HBM bytes per dispatch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs (no GPU)")
     return ap.parse_args()
@@ -153,6 +166,35 @@ def summarize_counters(prof_dir):
             "kernels": kernels}
 
 
+def summarize_pmc(prof_dir):
+    """Per-kernel averages per dispatch of every counter in rocprofv3 --pmc runs
+    under prof_dir (rows of one dispatch and counter are summed first), plus the
+    MFMA busy fraction SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * 256 CUs * 4
+    SIMDs) where both counters were collected in the same run."""
+    import csv
+    import glob
+    import re
+    per = {}
+    for f in glob.glob(os.path.join(prof_dir, "**", "*counter_collection.csv"), recursive=True):
+        run = os.path.relpath(os.path.dirname(f), prof_dir).split(os.sep)[0]
+        for r in csv.DictReader(open(f)):
+            name = re.sub(r"^void ", "", r["Kernel_Name"]).split("(")[0].split("<")[0].split("::")[-1]
+            key = (run, name, r["Counter_Name"])
+            disp = r.get("Dispatch_Id", r.get("Correlation_Id"))
+            per.setdefault(key, {}).setdefault(disp, 0.0)
+            per[key][disp] += float(r["Counter_Value"])
+    out = {}
+    for (run, name, ctr), d in sorted(per.items()):
+        out.setdefault(name, {}).setdefault(run, {})[ctr] = {"per_dispatch": sum(d.values()) / len(d),
+                                                             "dispatches": len(d)}
+    for name, runs in out.items():
+        for run, ctrs in runs.items():
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in ctrs and "GRBM_GUI_ACTIVE" in ctrs:
+                ctrs["mfma_busy_frac"] = (ctrs["SQ_VALU_MFMA_BUSY_CYCLES"]["per_dispatch"] /
+                                          (ctrs["GRBM_GUI_ACTIVE"]["per_dispatch"] * 256 * 4))
+    return out
+
+
 def calibrate_copy():
     import torch
     n = 256 << 20
@@ -188,6 +230,106 @@ def time_back_to_back(fn, n_calls, passes):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e-3 / (passes * n_calls)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on the host cores.
+
+def host_cores():
+    """Cores allotted to this process (capped by OMP_NUM_THREADS when it is set,
+    the host share that goes with one GPU) and the CPU model name."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def expert_jobs(ids, E):
+    """(expert, its tokens ascending) for every expert the routing selects, by id."""
+    jobs = []
+    for e in range(E):
+        tok = np.nonzero((ids == e).any(axis=1))[0].astype(np.int32)
+        if tok.size:
+            jobs.append((e, tok))
+    return jobs
+
+
+def run_jobs(jobs, work, threads, seconds=None):
+    """work(e, tokens) over the jobs in order on `threads` threads (the oracle's C
+    routines release the GIL while they run).  New jobs stop being started once
+    `seconds` have passed (None: run them all).  Returns (results in job order,
+    token pairs done, seconds)."""
+    import concurrent.futures as cf
+    t0 = time.perf_counter()
+    out, pairs = [], 0
+    if threads <= 1:
+        for e, tok in jobs:
+            out.append(work(e, tok))
+            pairs += tok.size
+            if seconds is not None and time.perf_counter() - t0 >= seconds:
+                break
+        return out, pairs, time.perf_counter() - t0
+    res = {}
+    with cf.ThreadPoolExecutor(threads) as ex:
+        pending, nxt = {}, 0
+        while nxt < len(jobs) and len(pending) < threads:
+            pending[ex.submit(work, *jobs[nxt])] = nxt
+            nxt += 1
+        while pending:
+            done, _ = cf.wait(pending, return_when=cf.FIRST_COMPLETED)
+            for f in done:
+                i = pending.pop(f)
+                res[i] = f.result()
+                pairs += jobs[i][1].size
+            while nxt < len(jobs) and len(pending) < threads and (
+                    seconds is None or time.perf_counter() - t0 < seconds):
+                pending[ex.submit(work, *jobs[nxt])] = nxt
+                nxt += 1
+    n = 0
+    while n in res:
+        n += 1
+    return [res[i] for i in range(n)], pairs, time.perf_counter() - t0
+
+
+def oracle_layer_threads(dtype, experts, x, logits, k, H, I, threads):
+    """One whole layer with the oracle's routines: top-k, then every selected
+    expert's rows (one oracle call per expert, spread over `threads` threads),
+    then y = sum_j w_tj * row(t, j) per token in increasing j (oracle combine)."""
+    import oracle
+    ids, _, w64 = oracle.route_topk(logits, k)
+    T = logits.shape[0]
+    jobs = expert_jobs(ids, logits.shape[1])
+    rows, _, _ = run_jobs(jobs, lambda e, tok: oracle.expert_rows(dtype, experts[e], H, I, x, tok), threads)
+    where = {}
+    for (e, tok), r in zip(jobs, rows):
+        for i, t in enumerate(tok):
+            where[(int(t), e)] = r[i]
+    gathered = np.array([[where[(t, int(ids[t, j]))] for j in range(k)] for t in range(T)])
+    return oracle.combine(gathered.reshape(T * k, H), w64)
+
+
+def cpu_threads(args):
+    """(threads of the all-core leg, CPU model)."""
+    n, model = host_cores()
+    return (args.cpu_threads or n), model
+
+
+def cpu_baseline_entry(single, multi, threads, model, unit):
+    """The cpu_baseline object: the all-core figure as the value, the single-thread
+    figure beside it."""
+    return dict(value=multi["value"], unit=unit, cores=threads, kind="oracle", sample=multi["sample"],
+                cpu_model=model, cores_allotted=len(os.sched_getaffinity(0)),
+                single_thread={"value": single["value"], "cores": 1, "sample": single["sample"]})
 
 
 # ---------------------------------------------------------------------------
@@ -303,10 +445,10 @@ def run_decode_bf16(T, n_layers, steps, warmup, time_kernel=True, eager=False):
     return res
 
 
-def cpu_decode_bf16(seconds):
-    """The oracle (plain fp64 C, one thread) on a bounded sample of the same
-    workload: decode layers of 16 tokens with the same shapes, until the budget
-    is spent."""
+def cpu_decode_bf16(seconds, threads, model):
+    """The oracle on a bounded sample of the same workload: decode layers of 16
+    tokens with the same shapes, whole layers until the budget is spent, on one
+    thread and on `threads` threads."""
     import synth
     import oracle
     c = synth.CONFIGS["decode_bf16"]
@@ -323,17 +465,24 @@ def cpu_decode_bf16(seconds):
     experts = [blank if v is None else v for v in experts]
     shared = synth.random_expert(synth.BF16, H, I, g)
     x = synth.encode_activations(synth.BF16, synth.normal_x(c["seed"], T, H, 99))
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.layer(synth.BF16, experts, x, logits, k, H, I, shared=shared, I_shared=I)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or n >= 50:
-            break
-    return dict(value=T * n / el, unit="layer-tokens/s", cores=1, kind="oracle",
-                sample=f"{n} decode layers of {T} tokens (H={H}, I={I}, {E} experts + shared, top-{k}), "
-                       f"fp64 C oracle, single thread, {el:.1f} s")
+    legs = {}
+    for nthr in (1, threads):
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            if nthr == 1:
+                oracle.layer(synth.BF16, experts, x, logits, k, H, I, shared=shared, I_shared=I)
+            else:
+                oracle_layer_threads(synth.BF16, experts, x, logits, k, H, I, nthr)
+                oracle.expert_rows(synth.BF16, shared, H, I, x, np.arange(T, dtype=np.int32))
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or n >= 50:
+                break
+        legs[nthr] = dict(value=T * n / el,
+                          sample=f"{n} decode layers of {T} tokens (H={H}, I={I}, {E} experts + shared, top-{k}) "
+                                 f"on {nthr} thread(s), {el:.1f} s")
+    return cpu_baseline_entry(legs[1], legs[threads], threads, model, "layer-tokens/s")
 
 
 def workload_decode_bf16(args):
@@ -350,7 +499,7 @@ def workload_decode_bf16(args):
             continue
         r = run_decode_bf16(tb, n_layers, max(10, steps // 2), 2, eager=args.eager)
         by_batch[str(tb)] = {k: r[k] for k in keys}
-    cpu = None if args.no_cpu_baseline else cpu_decode_bf16(args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline else cpu_decode_bf16(args.cpu_seconds, *cpu_threads(args))
     achieved = main_res["gate_up_gbs"]
     return out_line(
         main_res["layer_tokens_per_s"], "layer-tokens/s", steps, warmup, main_res["ms_per_step"], "bf16",
@@ -462,9 +611,11 @@ def run_decode_mxfp4(stack, c, T, n_layers, steps, warmup, n_batches=4, eager=Fa
                 down_avg_us=dn * 1e6, down_gbs=dnb / dn / 1e9, gate_up_launches_timed=passes * n_layers)
 
 
-def cpu_decode_mxfp4(stack, c, T, seconds):
+def cpu_decode_mxfp4(stack, c, T, seconds, threads, model):
     """The oracle on a bounded sample: MXFP4 decode layers of T tokens (layer 0's
-    experts, copied from HBM), until the budget is spent."""
+    experts, copied from HBM), whole layers until the budget is spent, on one
+    thread (the plain oracle layer) and on `threads` threads (its routines, one
+    call per expert)."""
     import synth
     import oracle
     H, I, E, k = c["H"], c["I"], c["E"], c["k"]
@@ -477,17 +628,23 @@ def cpu_decode_mxfp4(stack, c, T, seconds):
     for e in used:
         experts[e] = stack[e].cpu().numpy()
     x = synth.encode_activations(synth.BF16, synth.normal_x(c["seed"], T, H, 7, 0))
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.layer(synth.MXFP4, experts, x, logits, k, H, I)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or n >= 20:
-            break
-    return dict(value=T * n / el, unit="layer-tokens/s", cores=1, kind="oracle",
-                sample=f"{n} MXFP4 decode layers of {T} tokens ({len(used)} active experts of {E}, H={H}, I={I}, "
-                       f"top-{k}), fp64 C oracle, single thread, {el:.1f} s")
+    legs = {}
+    for nthr in (1, threads):
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            if nthr == 1:
+                oracle.layer(synth.MXFP4, experts, x, logits, k, H, I)
+            else:
+                oracle_layer_threads(synth.MXFP4, experts, x, logits, k, H, I, nthr)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or n >= 20:
+                break
+        legs[nthr] = dict(value=T * n / el,
+                          sample=f"{n} MXFP4 decode layers of {T} tokens ({len(used)} active experts of {E}, H={H}, "
+                                 f"I={I}, top-{k}) on {nthr} thread(s), {el:.1f} s")
+    return cpu_baseline_entry(legs[1], legs[threads], threads, model, "layer-tokens/s")
 
 
 def workload_decode_mxfp4(args):
@@ -508,7 +665,7 @@ def workload_decode_mxfp4(args):
         progress(f"decode_mxfp4: T={tb}")
         res[tb] = run_decode_mxfp4(stack, c, tb, n_layers, steps if tb == T else max(4, steps // 2), warmup,
                                    eager=args.eager)
-    cpu = None if args.no_cpu_baseline else cpu_decode_mxfp4(stack, c, 8, args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline else cpu_decode_mxfp4(stack, c, 8, args.cpu_seconds, *cpu_threads(args))
     m = res[T]
     keys = ("layer_tokens_per_s", "stack_tokens_per_s", "ms_per_step", "layer_hbm_gbs", "gate_up_gbs",
             "gate_up_avg_us", "down_gbs", "down_avg_us", "active_experts_mean")
@@ -661,9 +818,10 @@ def workload_prefill_mxfp4(args):
     layer_flop = gu_flop + dn_flop
     bp = host_to_device_gbs(lb, reps=3)
     ls.close()
-    cpu = None if args.no_cpu_baseline else cpu_prefill_mxfp4(banks[0], logits[0], xs[0], c, T, args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline else cpu_prefill_mxfp4(banks[0], logits[0], xs[0], c, T, args.cpu_seconds,
+                                                              *cpu_threads(args))
     gu_tf = gu_flop / gu / 1e12
-    return out_line(
+    line = out_line(
         T * n_layers / t_pipe, "layer-tokens/s", steps, warmup, t_pipe * 1e3, "bf16 (MXFP4 weights)",
         f"synthetic (seeded N(0,0.02) weights quantized to MXFP4, {n_host} distinct pinned host layers streamed "
         "as layer l mod that; N(0,1) logits and activations)",
@@ -684,13 +842,32 @@ def workload_prefill_mxfp4(args):
                       "tflops": layer_flop / (gu + dn) / 1e12,
                       "mfma_frac": layer_flop / (gu + dn) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                       "layer_tflops": layer_flop / (t_gemm / n_layers) / 1e12})
+    if not args.no_decode_leg:
+        del banks, host, b, xs, logits
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        line["decode_mxfp4"] = decode_leg(args)
+    return line
 
 
-def cpu_prefill_mxfp4(bank, logits_d, x_d, c, T, seconds):
-    """The oracle on a bounded sample of one prefill layer: routing of all T
-    tokens, then whole experts (each with all of its tokens) until the budget is
-    spent; the layer time is extrapolated from the measured seconds per routed
-    (token, expert) pair."""
+def decode_leg(args):
+    """The MXFP4 decode stack (43 layers, every expert resident; batch 64, then 1
+    and 8), measured after the prefill line in the same run: its own value,
+    roofline (gate_up against HBM) and CPU baseline."""
+    import argparse as ap
+    sub = ap.Namespace(**vars(args))
+    sub.tokens, sub.layers, sub.extra_batches = 64, None, "1,8"
+    sub.steps, sub.warmup = 10, 2
+    d = workload_decode_mxfp4(sub)
+    return {key: d[key] for key in ("value", "unit", "steps", "warmup", "ms_per_step", "dtype", "data", "config",
+                                    "roofline", "layer_hbm_frac", "by_batch", "cpu_baseline") if key in d}
+
+
+def cpu_prefill_mxfp4(bank, logits_d, x_d, c, T, seconds, threads, model):
+    """The oracle on a bounded sample of one prefill layer, on one thread and on
+    `threads` threads: routing of all T tokens, then whole experts (each with all
+    of its tokens, ascending expert id) until the budget is spent; the layer time
+    is extrapolated from the measured seconds per routed (token, expert) pair."""
     import synth
     import oracle
     H, I, E, k = c["H"], c["I"], c["E"], c["k"]
@@ -699,24 +876,21 @@ def cpu_prefill_mxfp4(bank, logits_d, x_d, c, T, seconds):
     t0 = time.perf_counter()
     ids, _, _ = oracle.route_topk(logits, k)
     t_route = time.perf_counter() - t0
-    pairs, t_ffn, n_exp = 0, 0.0, 0
-    for e in range(E):
-        tok = np.nonzero((ids == e).any(axis=1))[0].astype(np.int32)
-        if tok.size == 0:
-            continue
-        w = bank[e].cpu().numpy()
-        t0 = time.perf_counter()
-        oracle.expert_rows(synth.MXFP4, w, H, I, x, tok)
-        t_ffn += time.perf_counter() - t0
-        pairs += tok.size
-        n_exp += 1
-        if t_ffn >= seconds:
-            break
-    layer_s = t_route + t_ffn / pairs * T * k
-    return dict(value=T / layer_s, unit="layer-tokens/s", cores=1, kind="oracle",
-                sample=f"routing of {T} tokens + {n_exp} experts with {pairs} routed tokens of one MXFP4 prefill "
-                       f"layer (H={H}, I={I}), fp64 C oracle, single thread, {t_route + t_ffn:.1f} s; layer time "
-                       f"extrapolated to {T * k} routed tokens")
+    jobs = expert_jobs(ids, E)[:max(4, 6 * threads)]
+    weights = {e: bank[e].cpu().numpy() for e, _ in jobs}  # copied to the host before the timed calls
+
+    def work(e, tok):
+        return oracle.expert_rows(synth.MXFP4, weights[e], H, I, x, tok)
+
+    legs = {}
+    for n in (1, threads):
+        done, pairs, el = run_jobs(jobs, work, n, seconds)
+        layer_s = t_route + el / pairs * T * k
+        legs[n] = dict(value=T / layer_s,
+                       sample=f"routing of {T} tokens + {len(done)} experts with {pairs} routed tokens of one MXFP4 "
+                              f"prefill layer (H={H}, I={I}) on {n} thread(s), {t_route + el:.1f} s; layer time "
+                              f"extrapolated to {T * k} routed tokens")
+    return cpu_baseline_entry(legs[1], legs[threads], threads, model, "layer-tokens/s")
 
 
 # ---------------------------------------------------------------------------
@@ -795,7 +969,8 @@ def workload_cached_trace_bf16(args):
     progress(f"cached trace: {tokens} tokens in {el:.1f} s, miss rate {tot['misses'] / max(tot['accesses'], 1):.3f}")
     bp = host_to_device_gbs(eb)
     fill_gbs = tot["fill_bytes"] / el / 1e9
-    cpu = None if args.no_cpu_baseline else cpu_cached_trace(trace, host, c, n_layers, n_host, S, args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline else cpu_cached_trace(trace, host, c, n_layers, n_host, S, args.cpu_seconds,
+                                                             *cpu_threads(args))
     return out_line(
         tokens / el, "tokens/s", tokens, warm_tokens, el * 1e3 / tokens, "bf16",
         f"synthetic (seeded N(0,0.02) weights, {n_host} distinct pinned host layers serving layer l mod that; "
@@ -816,37 +991,46 @@ def workload_cached_trace_bf16(args):
         resize=resize)
 
 
-def cpu_cached_trace(trace, host, c, n_layers, n_host, S, seconds):
+def cpu_cached_trace(trace, host, c, n_layers, n_host, S, seconds, threads, model):
     """The oracle on the first tokens of the same trace: its global LRU plus the
-    layer for every (token, layer), until the budget is spent."""
+    layer for every (token, layer), until the budget is spent; on one thread and
+    with each layer's experts spread over `threads` threads."""
     import synth
     import oracle
     H, I, E, k = c["H"], c["I"], c["E"], c["k"]
     layers_host = [h.numpy() for h in host]
     xs = [synth.encode_activations(synth.BF16, synth.normal_x(c["seed"], 1, H, 7, l)) for l in range(n_layers)]
-    lru = oracle.LRU(S, n_layers, E)
-    n = 0
-    t0 = time.perf_counter()
-    while n < trace.shape[0]:
-        for l in range(n_layers):
-            lg = trace[n, l:l + 1]
-            ids, _, _ = oracle.route_topk(lg, k)
-            counts = np.bincount(ids.ravel(), minlength=E).astype(np.int32)
-            lru.step(l, counts)
-            oracle.layer(synth.BF16, layers_host[l % n_host], xs[l], lg, k, H, I)
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    el = time.perf_counter() - t0
-    return dict(value=n / el, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"first {n} tokens of the trace through {n_layers} layers (oracle LRU + layer), fp64 C "
-                       f"oracle, single thread, {el:.1f} s")
+    legs = {}
+    for nthr in (1, threads):
+        lru = oracle.LRU(S, n_layers, E)
+        n = 0
+        t0 = time.perf_counter()
+        while n < trace.shape[0]:
+            for l in range(n_layers):
+                lg = trace[n, l:l + 1]
+                ids, _, _ = oracle.route_topk(lg, k)
+                counts = np.bincount(ids.ravel(), minlength=E).astype(np.int32)
+                lru.step(l, counts)
+                if nthr == 1:
+                    oracle.layer(synth.BF16, layers_host[l % n_host], xs[l], lg, k, H, I)
+                else:
+                    oracle_layer_threads(synth.BF16, layers_host[l % n_host], xs[l], lg, k, H, I, nthr)
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        el = time.perf_counter() - t0
+        legs[nthr] = dict(value=n / el, sample=f"first {n} tokens of the trace through {n_layers} layers (oracle LRU "
+                                               f"+ layer) on {nthr} thread(s), {el:.1f} s")
+    return cpu_baseline_entry(legs[1], legs[threads], threads, model, "tokens/s")
 
 
 def main():
     args = parse()
     if args.summarize_counters:
         print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
+        return
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer runs on a single MI355X)",

@@ -81,8 +81,8 @@ const char* moe_last_error(void);
 size_t moe_expert_bytes(int wdt, int H, int I);
 
 /* ------------------------------------------------------------------------- */
-/* Top-k gating.  The pages: the engine follows the router and never modifies
- * it ("Three mechanisms": bandwidth-adaptive execution; "Key Takeaways").
+/* Top-k gating.  The pages: the model's own routing decides which experts run
+ * and the engine leaves it unchanged ("Three mechanisms": bandwidth-adaptive execution; "Key Takeaways").
  * For each token t: the k experts with the largest f32 logits, in descending
  * logit order, equal logits (IEEE equality, -0.0 == +0.0) going to the lower
  * expert index; gate weights are the softmax over the k selected logits (equal,
@@ -125,12 +125,13 @@ int moe_route_project(const void* x, const void* w_router, int T, int H, int E, 
                       int32_t* inv_rows, hipStream_t stream);
 
 /* ------------------------------------------------------------------------- */
-/* Expert-slot cache.  The pages: inactive experts sit in host memory and enter
- * the execution path on demand ("The gap it targets"); during decode a shared
- * LRU expert cache spanning all MoE layers follows the router ("Three
- * mechanisms": semantic-aware caching); experts are pinned in their final host
- * layout and the first request starts from a cold cache ("Three mechanisms":
- * elastic memory management).
+/* Expert-slot cache.  The pages: experts that are not in use are kept in host
+ * memory and brought to the GPU only when a token is routed to them ("The gap it
+ * targets"); in decode, one recency-ordered cache whose keys cover every MoE
+ * layer decides which experts stay on the GPU, driven by what the router picks
+ * ("Three mechanisms": semantic-aware caching); host copies of the experts are
+ * pinned in the layout the GPU computes from, and serving begins with nothing
+ * cached ("Three mechanisms": elastic memory management).
  *
  * Keys are (layer, expert), key = layer*n_experts + expert.  The cache starts
  * empty.  For one (step, layer) the active experts (counts > 0) are accessed
@@ -207,10 +208,12 @@ int moe_cache_lookup_fill_split(moe_cache* c, int layer, const int32_t* counts, 
  * keeps the min(n_slots, resident) most recently used keys, most recent first in
  * new slots 0, 1, ..., with their recency; the others are dropped (later accesses
  * miss).  Nothing is read from the host pool.  Device handle: slot_pool is the new
- * pool (n_slots * slot_stride bytes, stride >= expert_bytes and a multiple of 256,
- * not overlapping the current pool); in-flight fills are waited for, then each
- * kept expert is copied from its old slot on `stream` (after the work already on
- * it); the caller may free the old pool once that work is done.  Host-only handle:
+ * pool (256-byte aligned, n_slots * slot_stride bytes, stride >= expert_bytes and a
+ * multiple of 256, not overlapping the current pool); in-flight fills are waited
+ * for, then each kept expert is copied from its old slot on `stream` (after the
+ * work already on it); the next lookup makes its compute stream, and through it
+ * its fills, wait for those copies, so `stream` may differ from the compute
+ * stream; the caller may free the old pool once that work is done.  Host-only handle:
  * slot_pool must be NULL.  moved_from_host (nullable, [n_slots]) receives the old
  * slot of each new slot's expert, -1 for an empty slot.  On error the cache is
  * unchanged. */
@@ -258,6 +261,13 @@ int moe_grouped_ffn(int wdt, const void* slot_pool, size_t slot_stride, const in
                     const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
                     const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
                     float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream);
+/* Which kernel family moe_grouped_ffn runs for a shape (the results are the same
+ * computation either way): MOE_FFN_WEIGHT_STREAM (decode-sized batches: each
+ * expert's weights stream once past its few tokens) or MOE_FFN_GROUPED_GEMM
+ * (32 or more (token, expert) pairs per expert on average, bf16 or MXFP4 weights
+ * with H, I and I_shared multiples of 128).  -1 for an invalid shape. */
+enum { MOE_FFN_WEIGHT_STREAM = 0, MOE_FFN_GROUPED_GEMM = 1 };
+int moe_grouped_ffn_kind(int T, int k, int E, int H, int I, int I_shared, int wdt);
 /* The two phases of moe_grouped_ffn, same arguments: gate_up writes the SwiGLU
  * intermediate into the workspace, down reads it.  moe_grouped_ffn is exactly
  * gate_up followed by down on the same stream. */
@@ -281,9 +291,10 @@ int moe_combine(const float* out_rows, const float* topk_w, const int32_t* inv_r
                 int T, int k, int H, void* y, int ydt, hipStream_t stream);
 
 /* ------------------------------------------------------------------------- */
-/* Whole-layer streaming for prefill.  The pages: during prefill, full-layer
- * double buffering streams layer l+1 while the GPU computes layer l ("Three
- * mechanisms": semantic-aware caching).  Two device banks each hold one layer
+/* Whole-layer streaming for prefill.  The pages: in prefill, whole layers are
+ * copied into one of two device buffers, the next layer arriving while the
+ * current one is computed from the other ("Three mechanisms": semantic-aware
+ * caching).  Two device banks each hold one layer
  * (layer_bytes); a fill copies one layer from pinned host memory with one
  * hipMemcpyAsync on the fill stream.  Ordering: fill(bank) waits for the last
  * release(bank); acquire(bank) makes the compute stream wait for the last

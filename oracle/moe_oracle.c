@@ -4,8 +4,8 @@
  *
  * Pages: "Meet FreeToken: An Edge-Native MoE Serving Engine that Runs 753B GLM-5.2
  * on a Single Workstation GPU" (MarkTechPost).  The pages state the system's
- * policies (route without modifying the router, a shared LRU expert cache spanning
- * all MoE layers, a cold start, bit-exact expert output) but print no layer
+ * policies (routing left as the model has it, one LRU cache of experts keyed over
+ * every MoE layer, nothing cached at start, exact expert output) but print no layer
  * equation; every formula here is the textbook definition of the step, and each
  * reading the pages leave open is named where it is taken.
  *
@@ -347,10 +347,10 @@ int ora_layer(int dtype, const uint8_t* const* expert_ptr, const uint8_t* shared
 /* ===========================================================================
  * Global LRU expert cache
  *
- * The pages: during decode "a shared LRU expert cache spanning all MoE layers"
- * follows the router ("Three mechanisms", semantic-aware caching), and the first
- * request is served with a cold cache ("Three mechanisms", elastic memory
- * management).  Readings taken where they are silent:
+ * The pages: in decode, a single least-recently-used cache keyed over all MoE
+ * layers holds the experts the router keeps selecting ("Three mechanisms",
+ * semantic-aware caching), and nothing is cached when serving begins ("Three
+ * mechanisms", elastic memory management).  Readings taken where they are silent:
  *  - keys are (layer, expert), key = layer*E + expert; the cache starts empty;
  *  - within one (step, layer) the active experts are accessed hits first, then
  *    misses, each group in ascending expert id, hit/miss judged against the state

@@ -189,6 +189,14 @@ namespace {
 
 enum { PHASE_GATE_UP = 1, PHASE_DOWN = 2 };
 
+// Prefill-sized batches (32 or more pairs per expert on average) take the grouped
+// GEMM kernels, smaller ones the weight-streaming kernels; both compute the same
+// thing.
+constexpr int64_t kPrefillMinPairs = 32;
+bool uses_prefill(int wdt, int T, int k, int E, int H, int I, int I_shared) {
+  return (int64_t)T * k >= kPrefillMinPairs * E && moe::prefill_supported(wdt, H, I, I_shared);
+}
+
 int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, const int32_t* slot_of_expert,
                 const void* shared_w, int I_shared, const void* x, const int32_t* offsets, const int32_t* sorted_rows,
                 int T, int k, int E, int H, int I, float* out_rows, float* shared_out, void* workspace,
@@ -235,14 +243,7 @@ int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, 
   a.h_ld = I > I_shared ? I : I_shared;
   a.routed_items = (int)((int64_t)T * k < E ? (int64_t)T * k : E);
   a.lds_rows = 0;  // set per launch by the decode launchers
-  // Prefill-sized batches (32 or more pairs per expert on average) take the
-  // LDS-staged kernels; the results are the same computation.
-  // LDS-staged prefill kernels once experts carry MOE_PF_MIN_PAIRS token pairs on average.
-#ifndef MOE_PF_MIN_PAIRS
-#define MOE_PF_MIN_PAIRS 32
-#endif
-  const bool prefill =
-      (int64_t)T * k >= (int64_t)MOE_PF_MIN_PAIRS * E && moe::prefill_supported(wdt, H, I, I_shared);
+  const bool prefill = uses_prefill(wdt, T, k, E, H, I, I_shared);
   if (phases & PHASE_GATE_UP) {
     hipError_t e = prefill ? moe::launch_prefill_gate_up(wdt, a, stream) : moe::launch_ffn_gate_up(wdt, a, stream);
     if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn gate_up launch");
@@ -255,6 +256,12 @@ int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, 
 }
 
 }  // namespace
+
+int moe_grouped_ffn_kind(int T, int k, int E, int H, int I, int I_shared, int wdt) {
+  if (check_routing(T, E, k) || check_dims(wdt, H, I, "moe_grouped_ffn_kind")) return -1;
+  if (I_shared && check_dims(wdt, H, I_shared, "moe_grouped_ffn_kind shared expert")) return -1;
+  return uses_prefill(wdt, T, k, E, H, I, I_shared) ? MOE_FFN_GROUPED_GEMM : MOE_FFN_WEIGHT_STREAM;
+}
 
 int moe_grouped_ffn(int wdt, const void* slot_pool, size_t slot_stride, const int32_t* slot_of_expert,
                     const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
@@ -295,7 +302,9 @@ struct moe_cache {
   bool stage_used[8] = {};
   int stage_next = 0;
   hipEvent_t ev_counts = nullptr, ev_compute = nullptr, ev_fill = nullptr;
+  hipEvent_t ev_move = nullptr;           // end of the last resize's moves (on the caller's stream)
   bool fill_pending = false;              // a split lookup's fills not yet waited for
+  bool move_pending = false;              // a resize's moves not yet ordered before the compute stream
   int64_t fail_after = -1;                // injected failure: fills left before one fails
   std::vector<moe::PlannedFill> fills;
   std::vector<int32_t> table;
@@ -383,6 +392,7 @@ int moe_cache_create(const moe_cache_desc* d, moe_cache** out) {
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_counts, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fill, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_move, hipEventDisableTiming);
     for (int i = 0; i < kStages && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&c->stage_ev[i], hipEventDisableTiming);
     if (e != hipSuccess) {
       moe_cache_destroy(c);
@@ -409,6 +419,10 @@ int moe_cache_destroy(moe_cache* c) {
     if (c->ev_counts) (void)hipEventDestroy(c->ev_counts);
     if (c->ev_compute) (void)hipEventDestroy(c->ev_compute);
     if (c->ev_fill) (void)hipEventDestroy(c->ev_fill);
+    if (c->ev_move) {
+      if (c->move_pending) (void)hipEventSynchronize(c->ev_move);
+      (void)hipEventDestroy(c->ev_move);
+    }
     if (c->counts_pinned) (void)hipHostFree(c->counts_pinned);
     if (c->stage_pinned) (void)hipHostFree(c->stage_pinned);
   }
@@ -482,6 +496,13 @@ int lookup_fill_device(moe_cache* c, int layer, const int32_t* counts, int wave,
     e = hipStreamWaitEvent(compute_stream, c->ev_fill, 0);
     if (e != hipSuccess) return hip_fail(e, (std::string(what) + ": fencing earlier fills").c_str());
     c->fill_pending = false;
+  }
+  if (c->move_pending) {
+    // experts moved by a resize on another stream: the compute stream (and, through
+    // ev_compute, the fills of this lookup) come after the moves
+    e = hipStreamWaitEvent(compute_stream, c->ev_move, 0);
+    if (e != hipSuccess) return hip_fail(e, (std::string(what) + ": fencing a resize").c_str());
+    c->move_pending = false;
   }
   if (wave == 0) {
     if (!counts) return fail(MOE_EINVAL, "%s: null counts", what);
@@ -579,7 +600,8 @@ int moe_cache_resize(moe_cache* c, int n_slots, void* slot_pool, size_t slot_str
   std::vector<int32_t> moved;
   c->core.plan_resize(n_slots, moved);
   if (c->device) {
-    if (!slot_pool || !aligned16(slot_pool)) return fail(MOE_EINVAL, "moe_cache_resize: slot_pool must be a 16-byte aligned device pointer");
+    if (!slot_pool || ((uintptr_t)slot_pool & 255u) != 0)
+      return fail(MOE_EINVAL, "moe_cache_resize: slot_pool must be a 256-byte aligned device pointer");
     if (slot_stride < c->desc.expert_bytes || slot_stride % 256)
       return fail(MOE_EINVAL, "moe_cache_resize: slot_stride must be >= expert_bytes and a multiple of 256");
     const uintptr_t a0 = (uintptr_t)slot_pool, a1 = a0 + (uintptr_t)n_slots * slot_stride;
@@ -609,6 +631,9 @@ int moe_cache_resize(moe_cache* c, int n_slots, void* slot_pool, size_t slot_str
         if (e != hipSuccess) return hip_fail(e, "moe_cache_resize: moving an expert");
       }
     }
+    e = hipEventRecord(c->ev_move, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_cache_resize: recording the moves");
+    c->move_pending = true;
     c->desc.slot_pool = slot_pool;
     c->desc.slot_stride = slot_stride;
   } else if (slot_pool) {

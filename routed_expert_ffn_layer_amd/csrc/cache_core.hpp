@@ -1,9 +1,9 @@
 // cache_core.hpp -- host-side global LRU of the expert-slot cache (no HIP calls).
 //
 // Pages: "Meet FreeToken: An Edge-Native MoE Serving Engine that Runs 753B GLM-5.2
-// on a Single Workstation GPU" (MarkTechPost), "Three mechanisms": during decode a
-// shared LRU expert cache spanning all MoE layers follows the router; the first
-// request is served from a cold cache.
+// on a Single Workstation GPU" (MarkTechPost), "Three mechanisms": in decode, one
+// least-recently-used cache keyed over all MoE layers keeps the experts the router
+// selects; nothing is cached when serving begins.
 //
 // Policy (the pages leave the details open; this is the reading implemented):
 //  - keys are (layer, expert) -> layer*E + expert, one LRU over all layers;

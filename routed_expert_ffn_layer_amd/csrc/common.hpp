@@ -46,9 +46,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// E8M0 code -> the f32 multiplier 2^(s-127) (s = 0 is the subnormal 2^-127).
+// E8M0 code -> the f32 multiplier 2^(s-127) (s = 0 is the subnormal 2^-127; the
+// code 0xFF is NaN in OCP MX v1.0, and a NaN scale makes its whole block NaN).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-  return __uint_as_float(s == 0 ? 0x00400000u : (s << 23));
+  return __uint_as_float(s == 0 ? 0x00400000u : s == 255u ? 0x7fc00000u : (s << 23));
 }
 
 // 8 E2M1 codes (one 32-bit word, element 0 in the low nibble of byte 0) times the

@@ -54,7 +54,7 @@ EXPORTS = ["moe_abi_version", "moe_status_str", "moe_last_error", "moe_expert_by
            "moe_permute", "moe_cache_create", "moe_cache_destroy", "moe_cache_lookup_fill",
            "moe_cache_lookup_host", "moe_cache_state", "moe_cache_inject_fill_failure",
            "moe_cache_lookup_fill_split", "moe_cache_wait_fills", "moe_route", "moe_cache_resize", "moe_route_project",
-           "moe_grouped_ffn_workspace", "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down",
+           "moe_grouped_ffn_workspace", "moe_grouped_ffn_kind", "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down",
            "moe_combine", "moe_layer_stream_create", "moe_layer_stream_destroy", "moe_layer_stream_fill",
            "moe_layer_stream_acquire", "moe_layer_stream_release"]
 
@@ -88,6 +88,7 @@ def lib():
     L.moe_cache_state.argtypes = [P, P, P]
     L.moe_cache_inject_fill_failure.argtypes = [P, ctypes.c_int64]
     L.moe_grouped_ffn_workspace.restype = sz
+    L.moe_grouped_ffn_kind.argtypes = [i, i, i, i, i, i, i]
     L.moe_grouped_ffn_workspace.argtypes = [i, i, i, i, i, i, i]
     ffn_args = [i, P, sz, P, P, i, P, P, P, i, i, i, i, i, P, P, P, sz, P]
     L.moe_grouped_ffn.argtypes = ffn_args
@@ -156,6 +157,13 @@ def moe_permute(topk_ids, E, counts, offsets, sorted_rows, inv_rows, stream=None
 
 def moe_grouped_ffn_workspace(T, k, E, H, I, I_shared, wdt):
     return int(lib().moe_grouped_ffn_workspace(T, k, E, H, I, I_shared, wdt))
+
+
+MOE_FFN_WEIGHT_STREAM, MOE_FFN_GROUPED_GEMM = 0, 1
+
+
+def moe_grouped_ffn_kind(T, k, E, H, I, I_shared, wdt):
+    return int(lib().moe_grouped_ffn_kind(T, k, E, H, I, I_shared, wdt))
 
 
 def _ffn(fn, wdt, slot_pool, slot_stride, slot_of_expert, shared_w, I_shared, x, offsets, sorted_rows, T, k, E, H,

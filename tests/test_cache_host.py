@@ -150,3 +150,63 @@ def test_resize_between_steps_matches_oracle(ora):
     assert e.value.status == moe.MOE_ESTATE
     with pytest.raises(moe.MoeError):
         c.resize(0)
+
+
+def _ordered_dict_lru_misses(steps, S):
+    """Independent LRU (collections.OrderedDict, most recent last) over the same
+    access order: per step the hits ascending, then the misses ascending, hit or
+    miss judged before the step.  Returns (misses, resident keys oldest first)."""
+    from collections import OrderedDict
+    lru = OrderedDict()
+    misses = 0
+    for keys in steps:
+        hits = sorted(k for k in keys if k in lru)
+        miss = sorted(k for k in keys if k not in lru)
+        for k in hits:
+            lru.move_to_end(k)
+        for k in miss:
+            if len(lru) >= S:
+                lru.popitem(last=False)
+            lru[k] = True
+        misses += len(miss)
+    return misses, list(lru.keys())
+
+
+def test_cached_trace_full_matches_oracle(ora):
+    """The whole cached-trace workload: 1000 tokens x 48 layers x 256 experts, top-8,
+    4546 slots (37% of the pool), cold start.  The library's host handle and the
+    oracle make the same plan at every step (slots, fills, waves) and end in the
+    same state; their miss count equals an OrderedDict LRU's, and the cache runs
+    full and evicts (the first eviction comes after about 90 tokens)."""
+    cfg = synth.CONFIGS["cached_trace_bf16"]
+    E, L, k, S, n_tok = cfg["E"], cfg["layers"], cfg["k"], synth.cache_slots_for(cfg), cfg["tokens"]
+    assert S == 4546
+    lg = synth.trace_logits(cfg["seed"], n_tok, L, E, s=cfg["zipf_s"], reuse_p=cfg["reuse_p"])
+    ids, _, _ = ora.route_topk(lg.reshape(-1, E), k)
+    ids = ids.reshape(n_tok, L, k)
+    c = moe.MoeCache(L, E, S)
+    o = ora.LRU(S, L, E)
+    misses = accesses = 0
+    first_evict = None
+    steps = []
+    for t in range(n_tok):
+        for l in range(L):
+            counts = _counts(ids[t, l], E)
+            r = _step_both(c, o, l, counts, E, S)
+            accesses += len(r["expert"])
+            misses += int((r["hit"] == 0).sum())
+            if first_evict is None and misses > S:
+                first_evict = t
+            steps.append([l * E + int(e) for e in np.flatnonzero(counts)])
+    _same_state(c, o)
+    ref_misses, ref_keys = _ordered_dict_lru_misses(steps, S)
+    assert misses == ref_misses
+    keys, ticks = c.state()
+    order = [int(kk) for kk, _ in sorted((kk, tt) for kk, tt in zip(keys, ticks) if kk >= 0)]
+    assert sorted(order) == sorted(ref_keys)
+    by_tick = [int(kk) for tt, kk in sorted((tt, kk) for kk, tt in zip(keys, ticks) if kk >= 0)]
+    assert by_tick == ref_keys
+    assert accesses == n_tok * L * k
+    assert first_evict is not None and first_evict < n_tok // 2
+    print(f"cached trace: {misses} misses of {accesses} accesses ({misses / accesses:.2%}), "
+          f"first eviction at token {first_evict}")

@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import synth
-from helpers import (BF16_REL, F32_ATOL, W_ATOL, W_RTOL, assert_close_abs, assert_close_rel, bf16_to_f64,
+from helpers import (BF16_REL, F32_ATOL, W_ATOL, W_RTOL, assert_close_abs, assert_close_bf16_output, assert_close_rel,
+                     bf16_to_f64,
                      check_bf16_output, combine_f32, dev, log, pool_from_experts, run_resident_layer, to_dev)
 from routed_expert_ffn_layer_amd import layer as L
 from routed_expert_ffn_layer_amd import moe
@@ -142,49 +143,65 @@ def test_tiny_f32_layer(ora):
     _check_layer(ora, lay, b)
 
 
-# (dtype, T, H, I, E, k, shared): ragged token counts, several token tiles, more
-# than 128 tokens on one expert (two passes), K not a multiple of the MXFP4 step,
-# row-tile counts that leave a block partly filled.
+# (dtype, T, H, I, E, k, shared, logits, kernel family): ragged token counts,
+# several token tiles, more than 128 tokens on one expert (two passes), K not a
+# multiple of the MXFP4 step, row-tile counts that leave a block partly filled.
+# The kernel family (S: weight streaming, G: grouped GEMM) is asserted against the
+# library's dispatch for each case, so a case cannot silently change family.
 SMALL = [
-    (synth.BF16, 1, 256, 128, 16, 4, True),
-    (synth.BF16, 5, 256, 128, 16, 4, True),
-    (synth.BF16, 40, 512, 256, 32, 6, True),
-    (synth.BF16, 300, 256, 128, 2, 1, False),
-    (synth.BF16, 70, 128, 64, 4, 4, False),
-    (synth.MXFP4, 8, 512, 256, 8, 3, False),
-    (synth.MXFP4, 3, 160, 96, 8, 2, True),
-    (synth.MXFP4, 33, 256, 128, 16, 6, True),
-    (synth.MXFP4, 200, 128, 64, 2, 1, False),
-    (synth.MXFP4, 40, 160, 96, 8, 3, True),     # 4-tile down blocks over 10 row tiles: ragged last block
-    (synth.BF16, 20, 160, 96, 8, 3, True),
-    (synth.F32, 9, 64, 32, 5, 2, True),
-    # prefill-sized batches (>= 32 pairs per expert): LDS-staged kernels, token passes of 128
-    (synth.BF16, 512, 256, 256, 8, 2, False),
-    (synth.BF16, 300, 384, 128, 4, 2, True),
-    (synth.MXFP4, 600, 512, 256, 16, 4, True),
-    (synth.MXFP4, 257, 256, 384, 8, 1, False),
-    # MXFP4 decode with whole 16-step scale blocks (K = 2048): one and two token
-    # tiles, a shared expert whose down K (1024) is half a block, and 40 tokens per
-    # expert (two passes of at most 32)
-    (synth.MXFP4, 24, 2048, 2048, 4, 2, False),
-    (synth.MXFP4, 6, 2048, 2048, 3, 2, True),
-    (synth.MXFP4, 40, 2048, 2048, 2, 2, False),
+    (synth.BF16, 1, 256, 128, 16, 4, True, "normal", "S"),
+    (synth.BF16, 5, 256, 128, 16, 4, True, "normal", "S"),
+    (synth.BF16, 40, 512, 256, 32, 6, True, "normal", "S"),
+    (synth.BF16, 300, 256, 128, 2, 1, False, "normal", "G"),
+    (synth.BF16, 70, 128, 64, 4, 4, False, "normal", "S"),
+    (synth.MXFP4, 8, 512, 256, 8, 3, False, "normal", "S"),
+    (synth.MXFP4, 3, 160, 96, 8, 2, True, "normal", "S"),
+    (synth.MXFP4, 33, 256, 128, 16, 6, True, "normal", "S"),
+    (synth.MXFP4, 200, 128, 64, 2, 1, False, "normal", "S"),
+    (synth.MXFP4, 40, 160, 96, 8, 3, True, "normal", "S"),     # 4-tile down blocks over 10 row tiles: ragged last block
+    (synth.BF16, 20, 160, 96, 8, 3, True, "normal", "S"),
+    (synth.F32, 9, 64, 32, 5, 2, True, "normal", "S"),
+    # grouped GEMM (>= 32 pairs per expert on average, dimensions multiples of 128)
+    (synth.BF16, 512, 256, 256, 8, 2, False, "normal", "G"),
+    (synth.BF16, 300, 384, 128, 4, 2, True, "normal", "S"),
+    (synth.MXFP4, 600, 512, 256, 16, 4, True, "normal", "G"),
+    (synth.MXFP4, 257, 256, 384, 8, 1, False, "normal", "G"),
+    # grouped GEMM at H = 4096 (two MXFP4 scale blocks per gate_up row tile) with
+    # per-expert token counts 63..86, 90..109 and (Zipf-skewed) 5..166
+    (synth.MXFP4, 300, 4096, 256, 8, 2, False, "normal", "G"),
+    (synth.MXFP4, 400, 4096, 256, 8, 2, False, "normal", "G"),
+    (synth.MXFP4, 220, 4096, 256, 8, 2, True, "zipf", "G"),
+    (synth.BF16, 300, 4096, 256, 8, 2, False, "zipf", "G"),
+    # MXFP4 weight streaming with whole 16-step scale blocks (K = 2048): one and two
+    # token tiles, a shared expert whose down K (1024) is half a block, and a
+    # Zipf-skewed batch whose hottest expert carries 98 tokens (several passes)
+    (synth.MXFP4, 24, 2048, 2048, 4, 2, False, "normal", "S"),
+    (synth.MXFP4, 6, 2048, 2048, 3, 2, True, "normal", "S"),
+    (synth.MXFP4, 120, 2048, 512, 8, 2, False, "zipf", "S"),
     # token rows staged in LDS with K not a multiple of 128 (clamped columns), shared expert
-    (synth.MXFP4, 5, 160, 96, 8, 2, True),
+    (synth.MXFP4, 5, 160, 96, 8, 2, True, "normal", "S"),
     # H = 4096: the launch's LDS holds 5 token rows, so experts with more tokens (and
     # the shared expert) read theirs from memory in the same launch
-    (synth.MXFP4, 12, 4096, 256, 4, 2, True),
+    (synth.MXFP4, 12, 4096, 256, 4, 2, True, "normal", "S"),
 ]
 
 
-@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{synth.DTYPE_NAMES[c[0]]}_T{c[1]}_H{c[2]}_I{c[3]}_E{c[4]}_k{c[5]}_sh{int(c[6])}")
+def _small_id(c):
+    return f"{synth.DTYPE_NAMES[c[0]]}_T{c[1]}_H{c[2]}_I{c[3]}_E{c[4]}_k{c[5]}_sh{int(c[6])}_{c[7]}"
+
+
+@pytest.mark.parametrize("case", SMALL, ids=_small_id)
 def test_small_layers(ora, case):
-    dtype, T, H, I, E, k, shared = case
-    log(f"small layer {case}")
+    dtype, T, H, I, E, k, shared, logits, family = case
     I_sh = (I // 2 if dtype == synth.F32 else 32 * max(1, I // 64)) if shared else 0
-    lay = synth.small_layer(dtype, T, H, I, E, k, seed=500 + T, shared=shared, I_shared=I_sh)
+    kind = moe.moe_grouped_ffn_kind(T, k, E, H, I, I_sh, dtype)
+    assert kind == {"S": moe.MOE_FFN_WEIGHT_STREAM, "G": moe.MOE_FFN_GROUPED_GEMM}[family]
+    lay = synth.small_layer(dtype, T, H, I, E, k, seed=500 + T, shared=shared, I_shared=I_sh, logits=logits)
+    log(f"small layer {_small_id(case)} kind={kind}")
     b, *_ = run_resident_layer(lay)
-    _check_layer(ora, lay, b)
+    ref = _check_layer(ora, lay, b)
+    counts = np.bincount(ref["ids"].ravel(), minlength=E)
+    log(f"  tokens per expert {sorted(counts.tolist())}")
 
 
 def test_decode_bf16_full_shape(ora):
@@ -252,6 +269,62 @@ def test_decode_mxfp4_full_shape_sampled(ora):
             y_got.append(y_gpu[t])
         assert_close_rel(np.array(rows_got), np.array(rows_ref), BF16_REL, "sampled expert rows")
         assert_close_rel(np.array(y_got), np.array(y_ref), BF16_REL, "sampled y")
+
+
+def test_prefill_mxfp4_full_shape_sampled(ora):
+    """Prefill layer, MXFP4: H=4096, I=2048, 256 experts, top-6, T=4096 tokens with
+    N(0,1) logits (about 96 +- 10 tokens per expert, every expert active), through
+    the grouped GEMM kernels.  Routing and permutation are checked in full; every
+    output row of one expert per token-count class (49-64, 65-80, 81-96, 97-112,
+    113-128 tokens: 4 to 8 tiles of 16 tokens, 2 to 4 tiles of 32), and y of 8
+    tokens, against the oracle element by element."""
+    c = synth.CONFIGS["prefill_mxfp4"]
+    H, I, E, k, T = c["H"], c["I"], c["E"], c["k"], c["T"]
+    assert moe.moe_grouped_ffn_kind(T, k, E, H, I, 0, synth.MXFP4) == moe.MOE_FFN_GROUPED_GEMM
+    pool = synth.torch_mxfp4_expert_pool(E, H, I, seed=c["seed"], device=dev())
+    stride = pool.shape[1]
+    x = synth.encode_activations(synth.MXFP4, synth.normal_x(c["seed"], T, H, 0))
+    logits = synth.normal_logits(c["seed"], T, E, 0)
+    log(f"prefill mxfp4 full T={T}")
+    b = L.LayerBuffers(T, E, k, H, I, synth.MXFP4)
+    L.forward(b, to_dev(logits), to_dev(x), pool, stride, L.identity_slots(E))
+    torch.cuda.synchronize()
+    ids, _, w64 = ora.route_topk(logits, k)
+    np.testing.assert_array_equal(b.topk_ids.cpu().numpy(), ids)
+    rc, ro, rs, ri = ora.permute(ids, E)
+    np.testing.assert_array_equal(b.counts.cpu().numpy(), rc)
+    np.testing.assert_array_equal(b.offsets.cpu().numpy(), ro)
+    np.testing.assert_array_equal(b.sorted_rows.cpu().numpy()[: T * k], rs)
+    np.testing.assert_array_equal(b.inv_rows.cpu().numpy()[: T * k], ri)
+    out_rows = b.out_rows.cpu().numpy().astype(np.float64)
+    # one expert per token-count class, every one of its rows
+    chosen = []
+    for lo, hi in ((49, 64), (65, 80), (81, 96), (97, 112), (113, 128)):
+        cand = [e for e in range(E) if lo <= rc[e] <= hi]
+        if cand:
+            chosen.append(cand[len(cand) // 2])
+    assert len(chosen) >= 4, f"token counts {sorted(rc.tolist())} miss the classes"
+    for e in chosen:
+        toks = [int(r) // k for r in rs[ro[e]:ro[e + 1]]]
+        log(f"  expert {e}: {len(toks)} tokens")
+        ref = ora.expert_rows(synth.MXFP4, pool[e].cpu().numpy(), H, I, x, toks)
+        assert_close_rel(out_rows[ro[e]:ro[e + 1]], ref, BF16_REL, f"expert {e} rows ({len(toks)} tokens)")
+    # y of 8 tokens (all six experts of each)
+    y_gpu = combine_f32(b, False)
+    y_bf16 = bf16_to_f64(b.y)
+    sample = sorted(set([0, T - 1] + list(np.random.default_rng(7).choice(T, size=6, replace=False))))
+    by_expert = {}
+    for t in sample:
+        for j in range(k):
+            by_expert.setdefault(int(ids[t, j]), []).append(t)
+    o_ref = {}
+    for e, toks in by_expert.items():
+        for t, row in zip(toks, ora.expert_rows(synth.MXFP4, pool[e].cpu().numpy(), H, I, x, toks)):
+            o_ref[(t, e)] = row
+    y_ref = np.array([sum(w64[t, j] * o_ref[(t, int(ids[t, j]))] for j in range(k)) for t in sample])
+    r32 = assert_close_rel(y_gpu[sample], y_ref, BF16_REL, "sampled y (f32 output)")
+    r16 = assert_close_bf16_output(y_bf16[sample], y_ref, BF16_REL, "sampled y (bf16 output)")
+    log(f"  sampled y: max err / RMS = {r32:.2e} (f32 output), {r16:.2e} (bf16 output beyond its half-ulp)")
 
 
 def test_deterministic_and_doubling_invariant():

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import synth
-from helpers import assert_close_rel, dev, log, to_dev
+from helpers import assert_close_bf16_output, dev, log, to_dev
 from routed_expert_ffn_layer_amd import layer as L
 from routed_expert_ffn_layer_amd import moe
 
@@ -82,7 +82,8 @@ def test_streamed_layers_equal_resident(dtype, ora):
     # one streamed layer against the oracle
     lay = lays[3]
     ref = ora.layer(dtype, lay["experts"], lay["x"], lay["logits"], K, H, I)
-    assert_close_rel(ys[3].float().cpu().numpy(), ref["y"], what="streamed layer 3 vs oracle")
+    r = assert_close_bf16_output(ys[3].float().cpu().numpy(), ref["y"], what="streamed layer 3 vs oracle")
+    log(f"streamed layer 3: max err beyond the bf16 half-ulp / RMS = {r:.2e}")
 
 
 def test_streamed_layers_aliased_host(ora):
