@@ -60,6 +60,7 @@ def lib():
         L.ora_lru_free.restype = None
         L.ora_lru_free.argtypes = [P]
         L.ora_lru_step.argtypes = [P, i, P, P, P, P, P, P, P, P]
+        L.ora_lru_step_split.argtypes = [P, i, P, i, i, P, P, P, P, P, P, P, P, P, P]
         L.ora_lru_state.restype = None
         L.ora_lru_state.argtypes = [P, P, P]
         L.ora_router_logits.restype = i
@@ -210,19 +211,29 @@ class LRU:
             lib().ora_lru_free(self._h)
             self._h = None
 
-    def step(self, layer, counts):
+    def step(self, layer, counts, fill=None):
+        """One (step, layer); fill = (num, den) splits the misses (the first
+        floor(m num / den + 1/2) filled, the rest computed in place)."""
         counts = np.ascontiguousarray(counts, dtype=np.int32)
         E = self.E
         n = ctypes.c_int(0)
+        ni = ctypes.c_int(0)
         ex = np.empty(E, np.int32); hit = np.empty(E, np.int32); slot = np.empty(E, np.int32)
         wave = np.empty(E, np.int32); cold = np.empty(E, np.int32); ev = np.empty(E, np.int64)
-        nw = lib().ora_lru_step(self._h, layer, _p(counts), ctypes.byref(n), _p(ex), _p(hit), _p(slot),
-                                _p(wave), _p(cold), _p(ev))
+        inp = np.empty(E, np.int32); inp_cold = np.empty(E, np.int32)
+        if fill is None:
+            nw = lib().ora_lru_step(self._h, layer, _p(counts), ctypes.byref(n), _p(ex), _p(hit), _p(slot),
+                                    _p(wave), _p(cold), _p(ev))
+        else:
+            nw = lib().ora_lru_step_split(self._h, layer, _p(counts), int(fill[0]), int(fill[1]), ctypes.byref(n),
+                                          _p(ex), _p(hit), _p(slot), _p(wave), _p(cold), _p(ev), ctypes.byref(ni),
+                                          _p(inp), _p(inp_cold))
         if nw < 0:
             raise OracleError(f"ora_lru_step failed with {nw}")
         m = n.value
         return dict(expert=ex[:m].copy(), hit=hit[:m].copy(), slot=slot[:m].copy(), wave=wave[:m].copy(),
-                    cold=cold[:m].copy(), evicted=ev[:m].copy(), n_waves=nw)
+                    cold=cold[:m].copy(), evicted=ev[:m].copy(), n_waves=nw,
+                    inplace=inp[:ni.value].copy(), inplace_cold=inp_cold[:ni.value].copy())
 
     def state(self):
         keys = np.empty(self.S, np.int64)

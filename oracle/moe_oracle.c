@@ -413,17 +413,54 @@ static int lru_access(ora_lru* c, int64_t key, int* hit, int64_t* evicted) {
   return s;
 }
 
+/* Misses of a step that are filled into slots when the step has m misses and the
+ * fill fraction is num/den: q = floor(m * num / den + 1/2). */
+static int filled_misses(int m, int num, int den) { return (int)((2LL * m * num + den) / (2LL * den)); }
+
 int ora_lru_step(ora_lru* c, int layer, const int32_t* counts, int* n_access, int32_t* acc_expert,
                  int32_t* acc_hit, int32_t* acc_slot, int32_t* acc_wave, int32_t* acc_cold,
                  int64_t* acc_evicted) {
-  if (!c || layer < 0 || layer >= c->L) return -1;
-  int n = 0;
+  int n_inplace = 0;
+  return ora_lru_step_split(c, layer, counts, 1, 1, n_access, acc_expert, acc_hit, acc_slot, acc_wave, acc_cold,
+                            acc_evicted, &n_inplace, NULL, NULL);
+}
+
+/* The step with a split of its misses (the pages: of a step's misses, a share
+ * set by the host-link and host-memory bandwidths crosses the link into GPU
+ * memory and the rest is computed where the weights already sit, the partial
+ * sums merging exactly; "Three mechanisms", bandwidth-adaptive execution).  The
+ * one-GPU reading: of the m misses (ascending expert id), the first
+ * q = floor(m num / den + 1/2) are filled into slots as in ora_lru_step; the
+ * other m - q are computed in place from host memory and are not accessed: they
+ * take no slot, evict nothing and leave every tick as it was.  The cache sees the
+ * hits and the q filled misses only.  Outputs as ora_lru_step, plus the in-place
+ * experts (ascending id) and their cold flags (key never accessed before). */
+int ora_lru_step_split(ora_lru* c, int layer, const int32_t* counts, int fill_num, int fill_den, int* n_access,
+                       int32_t* acc_expert, int32_t* acc_hit, int32_t* acc_slot, int32_t* acc_wave,
+                       int32_t* acc_cold, int64_t* acc_evicted, int* n_inplace, int32_t* inplace_expert,
+                       int32_t* inplace_cold) {
+  if (!c || layer < 0 || layer >= c->L || fill_den < 1 || fill_num < 0 || fill_num > fill_den) return -1;
+  int n = 0, m = 0;
   /* hits first (state before the step), ascending expert id ... */
   for (int e = 0; e < c->E; ++e)
     if (counts[e] > 0 && c->slot_of_key[(int64_t)layer * c->E + e] >= 0) acc_expert[n++] = e;
-  /* ... then misses, ascending expert id */
+  /* ... then the misses, ascending expert id: the first q are accessed, the rest
+   * are computed in place */
   for (int e = 0; e < c->E; ++e)
-    if (counts[e] > 0 && c->slot_of_key[(int64_t)layer * c->E + e] < 0) acc_expert[n++] = e;
+    if (counts[e] > 0 && c->slot_of_key[(int64_t)layer * c->E + e] < 0) ++m;
+  const int q = filled_misses(m, fill_num, fill_den);
+  int seen_misses = 0, ni = 0;
+  for (int e = 0; e < c->E; ++e)
+    if (counts[e] > 0 && c->slot_of_key[(int64_t)layer * c->E + e] < 0) {
+      if (seen_misses++ < q) {
+        acc_expert[n++] = e;
+      } else {
+        if (inplace_expert) inplace_expert[ni] = e;
+        if (inplace_cold) inplace_cold[ni] = !c->seen[(int64_t)layer * c->E + e];
+        ++ni;
+      }
+    }
+  *n_inplace = ni;
   for (int a = 0; a < n; ++a) {
     int64_t key = (int64_t)layer * c->E + acc_expert[a];
     int hit;

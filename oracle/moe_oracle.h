@@ -80,6 +80,15 @@ void ora_lru_free(ora_lru* c);
 int ora_lru_step(ora_lru* c, int layer, const int32_t* counts, int* n_access, int32_t* acc_expert,
                  int32_t* acc_hit, int32_t* acc_slot, int32_t* acc_wave, int32_t* acc_cold,
                  int64_t* acc_evicted);
+/* The same step with its misses split: of the m misses (ascending expert id) the
+ * first floor(m * fill_num / fill_den + 1/2) are accessed (filled) as above; the
+ * others are computed in place and not accessed: listed in inplace_expert
+ * (nullable, room for E) with their cold flags (inplace_cold, nullable), count in
+ * *n_inplace.  0 <= fill_num <= fill_den, fill_den >= 1. */
+int ora_lru_step_split(ora_lru* c, int layer, const int32_t* counts, int fill_num, int fill_den, int* n_access,
+                       int32_t* acc_expert, int32_t* acc_hit, int32_t* acc_slot, int32_t* acc_wave,
+                       int32_t* acc_cold, int64_t* acc_evicted, int* n_inplace, int32_t* inplace_expert,
+                       int32_t* inplace_cold);
 /* key_of_slot [S] (layer*E + expert, -1 if empty) and last-use tick per slot. */
 void ora_lru_state(const ora_lru* c, int64_t* key_of_slot, int64_t* tick_of_slot);
 /* Elastic resize to new_S slots between steps: keeps the min(new_S, resident)

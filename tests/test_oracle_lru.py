@@ -23,10 +23,19 @@ class BruteLRU:
         self.slot = {}           # key -> slot
         self.seen = set()
 
-    def step(self, layer, E, counts):
+    def step(self, layer, E, counts, fill=None):
+        """fill = (num, den): of the m misses only the first floor(m num / den + 1/2)
+        are accessed; the others (self.inplace, with their cold flags) are not."""
         active = [e for e in range(E) if counts[e] > 0]
         resident = set(self.order)
-        seq = [e for e in active if layer * E + e in resident] + [e for e in active if layer * E + e not in resident]
+        misses = [e for e in active if layer * E + e not in resident]
+        self.inplace = []
+        if fill is not None:
+            from fractions import Fraction
+            q = math.floor(Fraction(len(misses) * fill[0], fill[1]) + Fraction(1, 2))
+            self.inplace = [(e, int(layer * E + e not in self.seen)) for e in misses[q:]]
+            misses = misses[:q]
+        seq = [e for e in active if layer * E + e in resident] + misses
         recs = []
         for a, e in enumerate(seq):
             key = layer * E + e
@@ -261,3 +270,72 @@ def test_lru_resize_closed_forms(ora):
     assert list(moved) == [0, -1, -1, -1]
     r = o.step(0, np.array([0, 0, 1, 1, 0, 0, 0, 0], np.int32))
     assert list(r["hit"]) == [1, 0] and list(r["slot"]) == [0, 1]
+
+
+# ---- the miss split: part of a step's misses computed in place, not accessed ----
+
+def _run_split(ora, S, L, E, steps, fill):
+    o = ora.LRU(S, L, E)
+    b = BruteLRU(S)
+    n_inplace = 0
+    for layer, counts in steps:
+        r = o.step(layer, counts, fill=fill)
+        recs = b.step(layer, E, counts, fill=fill)
+        got = list(zip(r["expert"], r["hit"], r["slot"], r["wave"], r["cold"], r["evicted"]))
+        assert [tuple(int(v) for v in g) for g in got] == recs
+        assert [(int(e), int(c)) for e, c in zip(r["inplace"], r["inplace_cold"])] == b.inplace
+        n_inplace += len(b.inplace)
+    keys, ticks = o.state()
+    res = {int(k): s for s, k in enumerate(keys) if k >= 0}
+    assert res == b.slot
+    assert [int(keys[s]) for s in np.argsort(ticks) if keys[s] >= 0] == b.order
+    return n_inplace
+
+
+@pytest.mark.parametrize("fill", [(0, 1), (1, 3), (1, 2), (2, 3), (3, 4), (1, 1)])
+def test_lru_split_matches_brute_force(ora, fill):
+    g = np.random.default_rng(5)
+    E, L = 16, 3
+    steps = []
+    for t in range(300):
+        ids = g.choice(E, size=g.integers(1, 7), replace=False)
+        steps.append((t % L, _counts_from_ids(ids, E)))
+    for S in (1, 3, 8, 20):
+        n = _run_split(ora, S, L, E, steps, fill)
+        assert (n == 0) == (fill == (1, 1))
+
+
+def test_lru_split_closed_forms(ora):
+    E = 8
+    # on an empty cache every active expert misses: the filled count follows the
+    # rounding rule floor(m num / den + 1/2) (halves round up)
+    for m, fill, q in ((1, (1, 2), 1), (3, (1, 2), 2), (1, (1, 3), 0), (2, (1, 3), 1), (5, (2, 5), 2),
+                       (4, (0, 1), 0), (4, (1, 1), 4), (7, (3, 4), 5)):
+        o = ora.LRU(4, 1, E)
+        r = o.step(0, _counts_from_ids(np.arange(m), E), fill=fill)
+        assert len(r["expert"]) == q and list(r["expert"]) == list(range(q))
+        assert list(r["inplace"]) == list(range(q, m)) and all(r["inplace_cold"] == 1)
+    # fill fraction 0: the cache never changes, every miss is computed in place
+    o = ora.LRU(5, 2, E)
+    g = np.random.default_rng(1)
+    for t in range(50):
+        r = o.step(t % 2, _counts_from_ids(g.choice(E, size=3, replace=False), E), fill=(0, 1))
+        assert len(r["expert"]) == 0 and len(r["inplace"]) == 3
+    keys, ticks = o.state()
+    assert np.all(keys == -1) and np.all(ticks == -1)
+    # fill fraction 1 is the unsplit step
+    o1, o2 = ora.LRU(6, 2, E), ora.LRU(6, 2, E)
+    for t in range(80):
+        c = _counts_from_ids(g.choice(E, size=int(g.integers(1, 5)), replace=False), E)
+        a, b = o1.step(t % 2, c), o2.step(t % 2, c, fill=(1, 1))
+        for key in ("expert", "hit", "slot", "wave", "cold", "evicted"):
+            assert np.array_equal(a[key], b[key])
+        assert len(b["inplace"]) == 0
+    assert all(np.array_equal(x, y) for x, y in zip(o1.state(), o2.state()))
+    # in-place keys are not accessed: a key computed in place misses again next step
+    # and is cold until it is filled once
+    o = ora.LRU(4, 1, E)
+    r = o.step(0, _counts_from_ids([2, 5], E), fill=(1, 2))
+    assert list(r["expert"]) == [2] and list(r["inplace"]) == [5]
+    r = o.step(0, _counts_from_ids([5], E), fill=(1, 1))
+    assert list(r["hit"]) == [0] and list(r["cold"]) == [1]
