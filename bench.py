@@ -74,6 +74,9 @@ def parse():
                          "graph per step, replayed)")
     ap.add_argument("--split-waves", action="store_true",
                     help="cached_trace_bf16: compute each wave's hits while its misses fill (default: after all fills)")
+    ap.add_argument("--fill-fraction", default=None, metavar="NUM/DEN",
+                    help="cached_trace_bf16: miss split; of each step's misses floor(m*NUM/DEN + 1/2) are filled, the "
+                         "rest computed in place from pinned host memory (default: every miss filled)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of each oracle CPU baseline leg (one thread, all cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -169,8 +172,10 @@ def summarize_counters(prof_dir):
 def summarize_pmc(prof_dir):
     """Per-kernel averages per dispatch of every counter in rocprofv3 --pmc runs
     under prof_dir (rows of one dispatch and counter are summed first), plus the
-    MFMA busy fraction SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * 256 CUs * 4
-    SIMDs) where both counters were collected in the same run."""
+    MFMA busy fraction SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs * 256 CUs
+    * 4 SIMDs) where both counters were collected in the same run (both arrive
+    summed over the GPU's instances: GRBM_GUI_ACTIVE once per XCD, the MFMA busy
+    cycles once per SIMD)."""
     import csv
     import glob
     import re
@@ -191,7 +196,7 @@ def summarize_pmc(prof_dir):
         for run, ctrs in runs.items():
             if "SQ_VALU_MFMA_BUSY_CYCLES" in ctrs and "GRBM_GUI_ACTIVE" in ctrs:
                 ctrs["mfma_busy_frac"] = (ctrs["SQ_VALU_MFMA_BUSY_CYCLES"]["per_dispatch"] /
-                                          (ctrs["GRBM_GUI_ACTIVE"]["per_dispatch"] * 256 * 4))
+                                          (ctrs["GRBM_GUI_ACTIVE"]["per_dispatch"] / 8 * 256 * 4))
     return out
 
 
@@ -926,14 +931,20 @@ def workload_cached_trace_bf16(args):
                            .view(np.int16)).to(dev) for l in range(n_layers)]
     b = L.LayerBuffers(1, E, k, H, I, moe.MOE_BF16)
 
-    fwd = L.forward_cached_split if args.split_waves else L.forward_cached
+    fill = None if args.fill_fraction is None else tuple(int(v) for v in args.fill_fraction.split("/"))
+    if fill is not None:
+        fwd = L.forward_cached_inplace
+    else:
+        fwd = L.forward_cached_split if args.split_waves else L.forward_cached
 
     def run(cache, n_tok):
-        tot = dict(accesses=0, hits=0, misses=0, fill_bytes=0, waves=0)
+        tot = dict(accesses=0, hits=0, misses=0, inplace=0, fill_bytes=0, waves=0)
+        if fill is not None:
+            cache.set_fill_fraction(*fill)
         for t in range(n_tok):
             for l in range(n_layers):
                 _, waves = fwd(b, cache, l, trace_d[t, l:l + 1], xs[l], slot_pool, stride)
-                for key in ("accesses", "hits", "misses"):  # per step, repeated by every wave's call
+                for key in ("accesses", "hits", "misses", "inplace"):  # per step, repeated by every wave's call
                     tot[key] += waves[0][key]
                 tot["fill_bytes"] += sum(w["fill_bytes"] for w in waves)
                 tot["waves"] += len(waves)
@@ -969,6 +980,7 @@ def workload_cached_trace_bf16(args):
     progress(f"cached trace: {tokens} tokens in {el:.1f} s, miss rate {tot['misses'] / max(tot['accesses'], 1):.3f}")
     bp = host_to_device_gbs(eb)
     fill_gbs = tot["fill_bytes"] / el / 1e9
+    link_gbs = (tot["fill_bytes"] + tot["inplace"] * eb) / el / 1e9
     cpu = None if args.no_cpu_baseline else cpu_cached_trace(trace, host, c, n_layers, n_host, S, args.cpu_seconds,
                                                              *cpu_threads(args))
     return out_line(
@@ -979,12 +991,18 @@ def workload_cached_trace_bf16(args):
                      "intermediate 512, global LRU over 37% of the experts", "tokens": tokens,
          "stacked_layers": n_layers, "slots": S, "slot_pool_gb": round(S * stride / 1e9, 2),
          "host_layers_distinct": n_host,
-         "waves": "split (hits computed while misses fill)" if args.split_waves else "whole (FFN after all fills)"},
-        {"kernel": "expert fills (hipMemcpyAsync pinned host -> HBM slots)", "bound": "pcie",
-         "achieved": fill_gbs, "peak": bp, "unit": "GB/s", "frac": fill_gbs / bp, "traffic": None,
-         "timing": "wall clock of the whole trace; peak = measured pinned host -> HBM bandwidth at one expert"},
+         "waves": ("miss split: hits, then in-place misses while the others fill" if fill is not None else
+                   "split (hits computed while misses fill)" if args.split_waves else "whole (FFN after all fills)"),
+         "fill_fraction": None if fill is None else f"{fill[0]}/{fill[1]}"},
+        {"kernel": "expert fills (hipMemcpyAsync pinned host -> HBM slots)" + (
+            " and in-place expert reads (FFN loads from pinned host memory)" if fill is not None else ""),
+         "bound": "pcie", "achieved": link_gbs, "peak": bp, "unit": "GB/s", "frac": link_gbs / bp, "traffic": None,
+         "timing": "wall clock of the whole trace; bytes over the host link (fills + in-place reads); peak = measured "
+                   "pinned host -> HBM bandwidth at one expert"},
         cpu, layer_tokens_per_s=tokens * n_layers / el,
         cache={"accesses": tot["accesses"], "hits": tot["hits"], "misses": tot["misses"],
+               "inplace": tot["inplace"], "inplace_bytes": tot["inplace"] * eb,
+               "link_gbs": (tot["fill_bytes"] + tot["inplace"] * eb) / el / 1e9,
                "miss_rate": tot["misses"] / max(tot["accesses"], 1), "fill_bytes": tot["fill_bytes"],
                "fill_gbs": fill_gbs, "host_to_device_gbs_one_expert": bp, "waves": tot["waves"],
                "expert_read_gbs": tot["accesses"] * eb / el / 1e9},

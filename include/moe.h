@@ -162,6 +162,7 @@ typedef struct {
   int64_t fill_bytes;   /* bytes copied by this call */
   int32_t n_waves;      /* waves this step needs */
   int32_t wave_accesses;/* accesses in the wave this call handled */
+  int64_t inplace;      /* misses of the step computed in place (miss split), not filled */
 } moe_cache_stats;
 
 typedef struct {
@@ -202,6 +203,31 @@ int moe_cache_lookup_fill(moe_cache* c, int layer, const int32_t* counts, int wa
  * must be 16-byte aligned and distinct. */
 int moe_cache_lookup_fill_split(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_hits,
                                 int32_t* slot_misses, moe_cache_stats* stats_host, hipStream_t compute_stream);
+/* Miss split (the pages: of a step's misses, a share set by the host-link and
+ * host-memory bandwidths crosses into GPU memory and the rest is computed where
+ * the weights already are, the partial sums merging exactly; "Three mechanisms",
+ * bandwidth-adaptive execution).  On one GPU "where the weights are" is pinned
+ * host memory read by the GPU in place.  With fill fraction num/den, of a step's
+ * m misses (ascending expert id) the first floor(m*num/den + 1/2) are filled as
+ * usual and the others are computed in place: they take no slot, evict nothing
+ * and leave the recency order as it is (hits are still refreshed).  Default 1/1
+ * (every miss filled).  Between steps only (MOE_ESTATE otherwise);
+ * 0 <= num <= den, den >= 1. */
+int moe_cache_set_fill_fraction(moe_cache* c, int num, int den);
+/* moe_cache_lookup_fill_split plus the step's in-place experts: addr_inplace
+ * (device [n_experts] uint64, 16-byte aligned) receives, with wave 0, the
+ * device-visible address of the pinned host copy of each in-place expert of the
+ * step (0 for every other expert, and everywhere for later waves), for
+ * moe_grouped_ffn_addr.  The host copies must be pinned memory the GPU can read
+ * (hipHostMalloc).  Same ordering rules as the split lookup; the in-place FFN can
+ * run while the fills are in flight (it reads only host memory). */
+int moe_cache_lookup_fill_inplace(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_hits,
+                                  int32_t* slot_misses, uint64_t* addr_inplace, moe_cache_stats* stats_host,
+                                  hipStream_t compute_stream);
+/* The in-place experts of the last step begun (ascending id); experts_host has
+ * room for n_experts.  Works on host-only and device handles. */
+int moe_cache_step_inplace(const moe_cache* c, int32_t* experts_host, int* n_host);
+
 /* Elastic resize of the slot pool (the pages: the expert pool grows and shrinks
  * with the memory the GPU can spare, "Three mechanisms", elastic memory
  * management).  Between steps only (MOE_ESTATE while a step's waves are open):
@@ -261,6 +287,16 @@ int moe_grouped_ffn(int wdt, const void* slot_pool, size_t slot_stride, const in
                     const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
                     const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
                     float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream);
+/* moe_grouped_ffn over experts addressed one by one instead of through slots:
+ * expert_addr (device [E] uint64) holds the address of each expert's weights
+ * (same layout as a slot; 16-byte aligned; device memory or pinned host memory
+ * the GPU can read), 0 for experts not computed by this call.  Used for the
+ * in-place half of the miss split; the results for an expert are bit for bit
+ * those of moe_grouped_ffn on a slot holding the same bytes. */
+int moe_grouped_ffn_addr(int wdt, const uint64_t* expert_addr, const void* shared_w, int I_shared, const void* x,
+                         const int32_t* offsets, const int32_t* sorted_rows, int T, int k, int E, int H, int I,
+                         float* out_rows, float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Which kernel family moe_grouped_ffn runs for a shape (the results are the same
  * computation either way): MOE_FFN_WEIGHT_STREAM (decode-sized batches: each
  * expert's weights stream once past its few tokens) or MOE_FFN_GROUPED_GEMM

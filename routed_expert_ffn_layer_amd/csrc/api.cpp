@@ -200,7 +200,7 @@ bool uses_prefill(int wdt, int T, int k, int E, int H, int I, int I_shared) {
 int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, const int32_t* slot_of_expert,
                 const void* shared_w, int I_shared, const void* x, const int32_t* offsets, const int32_t* sorted_rows,
                 int T, int k, int E, int H, int I, float* out_rows, float* shared_out, void* workspace,
-                size_t ws_bytes, hipStream_t stream) {
+                size_t ws_bytes, hipStream_t stream, const uint64_t* expert_addr = nullptr) {
   if (int rc = check_routing(T, E, k)) return rc;
   if (int rc = check_dims(wdt, H, I, "moe_grouped_ffn")) return rc;
   if (shared_w) {
@@ -211,22 +211,28 @@ int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, 
     I_shared = 0;
   }
   if (T == 0) return MOE_OK;
-  REQUIRE_PTR(slot_pool);
-  REQUIRE_PTR(slot_of_expert);
+  if (expert_addr) {
+    REQUIRE_PTR(expert_addr);
+  } else {
+    REQUIRE_PTR(slot_pool);
+    REQUIRE_PTR(slot_of_expert);
+  }
   REQUIRE_PTR(x);
   REQUIRE_PTR(offsets);
   REQUIRE_PTR(sorted_rows);
   REQUIRE_PTR(out_rows);
   REQUIRE_PTR(workspace);
   const size_t eb = moe_expert_bytes(wdt, H, I);
-  REQUIRE(slot_stride >= eb && slot_stride % 16 == 0,
-          "slot_stride=%zu must be >= expert bytes %zu and a multiple of 16", slot_stride, eb);
+  if (!expert_addr)
+    REQUIRE(slot_stride >= eb && slot_stride % 16 == 0,
+            "slot_stride=%zu must be >= expert bytes %zu and a multiple of 16", slot_stride, eb);
   const size_t need = moe::ffn_workspace_bytes(wdt, T, k, I, I_shared);
   if (ws_bytes < need) return fail(MOE_ECAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, need);
   moe::FfnArgs a;
   a.slot_pool = static_cast<const uint8_t*>(slot_pool);
   a.slot_stride = slot_stride;
-  a.slot_of_expert = slot_of_expert;
+  a.slot_of_expert = expert_addr ? nullptr : slot_of_expert;
+  a.expert_addr = expert_addr;
   a.shared_w = static_cast<const uint8_t*>(shared_w);
   a.x = x;
   a.offsets = offsets;
@@ -256,6 +262,13 @@ int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, 
 }
 
 }  // namespace
+
+int moe_grouped_ffn_addr(int wdt, const uint64_t* expert_addr, const void* shared_w, int I_shared, const void* x,
+                         const int32_t* offsets, const int32_t* sorted_rows, int T, int k, int E, int H, int I,
+                         float* out_rows, float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return grouped_ffn(PHASE_GATE_UP | PHASE_DOWN, wdt, nullptr, 0, nullptr, shared_w, I_shared, x, offsets, sorted_rows,
+                     T, k, E, H, I, out_rows, shared_out, workspace, ws_bytes, stream, expert_addr);
+}
 
 int moe_grouped_ffn_kind(int T, int k, int E, int H, int I, int I_shared, int wdt) {
   if (check_routing(T, E, k) || check_dims(wdt, H, I, "moe_grouped_ffn_kind")) return -1;
@@ -298,6 +311,8 @@ struct moe_cache {
   bool device = false;
   int32_t* counts_pinned = nullptr;       // [E]
   int32_t* stage_pinned = nullptr;        // [kStages][2E] (a split lookup uploads two tables)
+  uint64_t* stage_addr_pinned = nullptr;  // [kStages][E] (in-place expert addresses)
+  std::vector<uint64_t> dev_addr;         // [L*E] device-visible address of each host copy (0: not looked up)
   hipEvent_t stage_ev[8] = {};
   bool stage_used[8] = {};
   int stage_next = 0;
@@ -309,7 +324,11 @@ struct moe_cache {
   std::vector<moe::PlannedFill> fills;
   std::vector<int32_t> table;
 
-  moe_cache(const moe_cache_desc& d) : core(d.n_slots, d.n_layers, d.n_experts), desc(d), table(d.n_experts) {}
+  moe_cache(const moe_cache_desc& d)
+      : core(d.n_slots, d.n_layers, d.n_experts),
+        desc(d),
+        dev_addr((size_t)d.n_layers * d.n_experts, 0),
+        table(d.n_experts) {}
 };
 
 namespace {
@@ -331,6 +350,7 @@ void fill_stats(const moe_cache* c, int nacc, int64_t bytes, moe_cache_stats* st
   st->fill_bytes = bytes;
   st->n_waves = s.n_waves;
   st->wave_accesses = nacc;
+  st->inplace = s.inplace;
 }
 
 // Shared between the host and device lookups: open/validate the step and plan the wave.
@@ -389,6 +409,9 @@ int moe_cache_create(const moe_cache_desc* d, moe_cache** out) {
     hipError_t e = hipHostMalloc((void**)&c->counts_pinned, sizeof(int32_t) * d->n_experts, hipHostMallocDefault);
     if (e == hipSuccess)
       e = hipHostMalloc((void**)&c->stage_pinned, sizeof(int32_t) * 2 * d->n_experts * kStages, hipHostMallocDefault);
+    if (e == hipSuccess)
+      e = hipHostMalloc((void**)&c->stage_addr_pinned, sizeof(uint64_t) * d->n_experts * kStages,
+                        hipHostMallocDefault);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_counts, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fill, hipEventDisableTiming);
@@ -425,6 +448,7 @@ int moe_cache_destroy(moe_cache* c) {
     }
     if (c->counts_pinned) (void)hipHostFree(c->counts_pinned);
     if (c->stage_pinned) (void)hipHostFree(c->stage_pinned);
+    if (c->stage_addr_pinned) (void)hipHostFree(c->stage_addr_pinned);
   }
   delete c;
   return rc;
@@ -481,13 +505,15 @@ namespace {
 // the wave's misses) and `slot_misses` the filled experts only, and the compute
 // stream waits for the fills only at moe_cache_wait_fills.
 int lookup_fill_device(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_a,
-                       int32_t* slot_misses, moe_cache_stats* stats_host, hipStream_t compute_stream,
-                       const char* what) {
+                       int32_t* slot_misses, uint64_t* addr_inplace, moe_cache_stats* stats_host,
+                       hipStream_t compute_stream, const char* what) {
   if (!c) return fail(MOE_EINVAL, "null cache");
   if (!c->device) return fail(MOE_EINVAL, "%s needs a device cache (slot_pool set)", what);
   if (!slot_a || !aligned16(slot_a)) return fail(MOE_EINVAL, "%s: slot table must be a 16-byte aligned pointer", what);
   if (slot_misses && !aligned16(slot_misses))
     return fail(MOE_EINVAL, "%s: slot_misses must be a 16-byte aligned pointer", what);
+  if (addr_inplace && !aligned16(addr_inplace))
+    return fail(MOE_EINVAL, "%s: addr_inplace must be a 16-byte aligned pointer", what);
   const bool split = slot_misses != nullptr;
   const int E = c->desc.n_experts;
   hipError_t e;
@@ -514,6 +540,35 @@ int lookup_fill_device(moe_cache* c, int layer, const int32_t* counts, int wave,
   }
   int nacc = 0;
   if (int rc = plan(c, layer, c->counts_pinned, wave, &nacc)) return rc;
+  // device-visible addresses of the step's in-place experts (reported with wave 0)
+  const int q = c->stage_next;
+  if (addr_inplace) {
+    if (c->stage_used[q]) {
+      e = hipEventSynchronize(c->stage_ev[q]);
+      if (e != hipSuccess) {
+        c->core.abort_step();
+        return hip_fail(e, (std::string(what) + ": staging buffer").c_str());
+      }
+      c->stage_used[q] = false;
+    }
+    uint64_t* stage_addr = c->stage_addr_pinned + (size_t)q * E;
+    for (int x = 0; x < E; ++x) stage_addr[x] = 0;
+    if (wave == 0)
+      for (int x : c->core.inplace()) {
+        const int64_t key = (int64_t)layer * E + x;
+        if (!c->dev_addr[key]) {
+          void* d = nullptr;
+          e = hipHostGetDevicePointer(&d, const_cast<void*>(host_src(c, layer, x)), 0);
+          if (e != hipSuccess || !d) {
+            c->core.abort_step();
+            return hip_fail(e != hipSuccess ? e : hipErrorInvalidValue,
+                            (std::string(what) + ": host copy of an in-place expert is not device-visible").c_str());
+          }
+          c->dev_addr[key] = (uint64_t)(uintptr_t)d;
+        }
+        stage_addr[x] = c->dev_addr[key];
+      }
+  }
   int64_t bytes = 0;
   if (!c->fills.empty()) {
     // write-after-read: victims may still be read by FFN work already enqueued
@@ -549,7 +604,6 @@ int lookup_fill_device(moe_cache* c, int layer, const int32_t* counts, int wave,
   }
   c->core.commit_wave(wave);
   // slot table(s) upload through a ring of pinned staging buffers
-  const int q = c->stage_next;
   c->stage_next = (q + 1) % kStages;
   if (c->stage_used[q]) {
     e = hipEventSynchronize(c->stage_ev[q]);
@@ -568,6 +622,9 @@ int lookup_fill_device(moe_cache* c, int layer, const int32_t* counts, int wave,
   e = hipMemcpyAsync(slot_a, stage, sizeof(int32_t) * E, hipMemcpyHostToDevice, compute_stream);
   if (e == hipSuccess && split)
     e = hipMemcpyAsync(slot_misses, stage + E, sizeof(int32_t) * E, hipMemcpyHostToDevice, compute_stream);
+  if (e == hipSuccess && addr_inplace)
+    e = hipMemcpyAsync(addr_inplace, c->stage_addr_pinned + (size_t)q * E, sizeof(uint64_t) * E,
+                       hipMemcpyHostToDevice, compute_stream);
   if (e == hipSuccess) e = hipEventRecord(c->stage_ev[q], compute_stream);
   if (e != hipSuccess) return hip_fail(e, (std::string(what) + ": slot table upload").c_str());
   c->stage_used[q] = true;
@@ -581,15 +638,40 @@ extern "C" {
 
 int moe_cache_lookup_fill(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_of_expert,
                           moe_cache_stats* stats_host, hipStream_t compute_stream) {
-  return lookup_fill_device(c, layer, counts, wave, slot_of_expert, nullptr, stats_host, compute_stream,
+  return lookup_fill_device(c, layer, counts, wave, slot_of_expert, nullptr, nullptr, stats_host, compute_stream,
                             "moe_cache_lookup_fill");
 }
 
 int moe_cache_lookup_fill_split(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_hits,
                                 int32_t* slot_misses, moe_cache_stats* stats_host, hipStream_t compute_stream) {
   if (!slot_misses) return fail(MOE_EINVAL, "moe_cache_lookup_fill_split: null slot_misses");
-  return lookup_fill_device(c, layer, counts, wave, slot_hits, slot_misses, stats_host, compute_stream,
+  return lookup_fill_device(c, layer, counts, wave, slot_hits, slot_misses, nullptr, stats_host, compute_stream,
                             "moe_cache_lookup_fill_split");
+}
+
+int moe_cache_lookup_fill_inplace(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_hits,
+                                  int32_t* slot_misses, uint64_t* addr_inplace, moe_cache_stats* stats_host,
+                                  hipStream_t compute_stream) {
+  if (!slot_misses || !addr_inplace) return fail(MOE_EINVAL, "moe_cache_lookup_fill_inplace: null table");
+  return lookup_fill_device(c, layer, counts, wave, slot_hits, slot_misses, addr_inplace, stats_host,
+                            compute_stream, "moe_cache_lookup_fill_inplace");
+}
+
+int moe_cache_set_fill_fraction(moe_cache* c, int num, int den) {
+  if (!c) return fail(MOE_EINVAL, "null cache");
+  if (den < 1 || num < 0 || num > den)
+    return fail(MOE_EINVAL, "moe_cache_set_fill_fraction: need 0 <= num <= den and den >= 1 (got %d/%d)", num, den);
+  if (c->core.step_open()) return fail(MOE_ESTATE, "moe_cache_set_fill_fraction: a step is still open");
+  c->core.set_fill_fraction(num, den);
+  return MOE_OK;
+}
+
+int moe_cache_step_inplace(const moe_cache* c, int32_t* experts_host, int* n_host) {
+  if (!c || !experts_host || !n_host) return fail(MOE_EINVAL, "moe_cache_step_inplace: null argument");
+  const std::vector<int32_t>& v = c->core.inplace();
+  for (size_t i = 0; i < v.size(); ++i) experts_host[i] = v[i];
+  *n_host = (int)v.size();
+  return MOE_OK;
 }
 
 int moe_cache_resize(moe_cache* c, int n_slots, void* slot_pool, size_t slot_stride, int32_t* moved_from_host,

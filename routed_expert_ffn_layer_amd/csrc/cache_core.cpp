@@ -59,13 +59,23 @@ void LruCore::begin_step(int layer, const int32_t* counts) {
   for (int e = 0; e < E_; ++e)
     if (counts[e] > 0 && slot_of_key_[base + e] >= 0) order_.push_back(e);
   stats_.hits = (int64_t)order_.size();
+  inplace_.clear();
+  int64_t m = 0;
+  for (int e = 0; e < E_; ++e)
+    if (counts[e] > 0 && slot_of_key_[base + e] < 0) ++m;
+  const int64_t q = (2 * m * fill_num_ + fill_den_) / (2 * (int64_t)fill_den_);
+  int64_t i = 0;
   for (int e = 0; e < E_; ++e)
     if (counts[e] > 0 && slot_of_key_[base + e] < 0) {
-      order_.push_back(e);
+      if (i++ < q)
+        order_.push_back(e);
+      else
+        inplace_.push_back(e);
       stats_.cold_misses += seen_[base + e] ? 0 : 1;
     }
-  stats_.accesses = (int64_t)order_.size();
-  stats_.misses = stats_.accesses - stats_.hits;
+  stats_.misses = m;
+  stats_.inplace = m - q;
+  stats_.accesses = stats_.hits + m;
   stats_.n_waves = order_.empty() ? 0 : (int32_t)((order_.size() - 1) / S_ + 1);
   next_wave_ = 0;
   step_open_ = true;

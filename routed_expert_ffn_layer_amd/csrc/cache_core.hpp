@@ -10,7 +10,10 @@
 //  - a step's active experts are accessed hits first, then misses, each in
 //    ascending expert id, hit/miss judged against the state before the step;
 //  - a miss takes the lowest-index free slot, else the least recently used key's;
-//  - more active experts than slots -> consecutive waves of n_slots accesses.
+//  - more active experts than slots -> consecutive waves of n_slots accesses;
+//  - miss split (fill fraction num/den, default 1): of the step's m misses the
+//    first floor(m num / den + 1/2) (ascending id) are accessed and filled, the
+//    others are computed in place from host memory and not accessed at all.
 //
 // Data structures: key -> slot array over all keys, an intrusive doubly linked
 // recency list over slots (head = least recent) with a strictly increasing tick,
@@ -34,7 +37,7 @@ struct PlannedFill {
 };
 
 struct StepStats {
-  int64_t accesses = 0, hits = 0, misses = 0, cold_misses = 0;
+  int64_t accesses = 0, hits = 0, misses = 0, cold_misses = 0, inplace = 0;
   int32_t n_waves = 0;
 };
 
@@ -46,8 +49,16 @@ class LruCore {
   int n_layers() const { return L_; }
   int n_experts() const { return E_; }
 
+  // Fill fraction of the miss split (0 <= num <= den, den >= 1); between steps.
+  void set_fill_fraction(int num, int den) {
+    fill_num_ = num;
+    fill_den_ = den;
+  }
   // Start a step for `layer`: builds the access order from counts (host, [E]).
   void begin_step(int layer, const int32_t* counts);
+  // Misses of the open (or last) step computed in place, ascending id.
+  const std::vector<int32_t>& inplace() const { return inplace_; }
+  int layer() const { return layer_; }
   bool step_open() const { return step_open_; }
   int next_wave() const { return next_wave_; }
   const StepStats& step_stats() const { return stats_; }
@@ -91,7 +102,9 @@ class LruCore {
   int layer_ = 0;
   int next_wave_ = 0;
   std::vector<int32_t> order_;  // experts in access order
+  std::vector<int32_t> inplace_;
   StepStats stats_;
+  int fill_num_ = 1, fill_den_ = 1;
 };
 
 }  // namespace moe

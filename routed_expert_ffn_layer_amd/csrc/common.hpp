@@ -20,7 +20,8 @@ enum WType { W_F32 = 0, W_BF16 = 1, W_MXFP4 = 2 };
 struct FfnArgs {
   const uint8_t* slot_pool;
   uint64_t slot_stride;
-  const int32_t* slot_of_expert;  // [E]
+  const int32_t* slot_of_expert;  // [E] slot of each expert (-1: not computed), or null when expert_addr is set
+  const uint64_t* expert_addr;    // [E] address of each expert's weights (0: not computed), or null
   const uint8_t* shared_w;        // nullable
   const void* x;                  // [T][H] f32 or bf16
   const int32_t* offsets;         // [E+1]
@@ -99,12 +100,13 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 // Item resolution for the grouped FFN.  The a-th expert (ascending id) that has
-// pairs and a slot in this call.  Every lane of the wave gets the same answer.
+// pairs and a slot (or a non-zero weight address) in this call.  Every lane of the wave gets the same answer.
 // Returns -1 if fewer than a+1 experts are active.  All loads are issued before
 // the scan, so the lookup costs one memory round trip.
 template <int EPL>
 __device__ __forceinline__ int nth_active_expert_t(const int32_t* __restrict__ offsets,
-                                                   const int32_t* __restrict__ slot_of_expert, int E, int a) {
+                                                   const int32_t* __restrict__ slot_of_expert,
+                                                   const uint64_t* __restrict__ expert_addr, int E, int a) {
   const int lane = threadIdx.x & 63;
   int lo[EPL], hi[EPL], sl[EPL];
 #pragma unroll
@@ -113,7 +115,10 @@ __device__ __forceinline__ int nth_active_expert_t(const int32_t* __restrict__ o
     const bool in = e < E;
     lo[i] = in ? offsets[e] : 0;
     hi[i] = in ? offsets[e + 1] : 0;
-    sl[i] = in ? slot_of_expert[e] : -1;
+    if (expert_addr)
+      sl[i] = in && expert_addr[e] != 0 ? 0 : -1;
+    else
+      sl[i] = in ? slot_of_expert[e] : -1;
   }
   int base = 0;
 #pragma unroll
@@ -131,12 +136,13 @@ __device__ __forceinline__ int nth_active_expert_t(const int32_t* __restrict__ o
 }
 
 __device__ __forceinline__ int nth_active_expert(const int32_t* __restrict__ offsets,
-                                                 const int32_t* __restrict__ slot_of_expert, int E, int a) {
-  if (E <= 64) return nth_active_expert_t<1>(offsets, slot_of_expert, E, a);
-  if (E <= 128) return nth_active_expert_t<2>(offsets, slot_of_expert, E, a);
-  if (E <= 256) return nth_active_expert_t<4>(offsets, slot_of_expert, E, a);
-  if (E <= 512) return nth_active_expert_t<8>(offsets, slot_of_expert, E, a);
-  return nth_active_expert_t<16>(offsets, slot_of_expert, E, a);
+                                                 const int32_t* __restrict__ slot_of_expert,
+                                                 const uint64_t* __restrict__ expert_addr, int E, int a) {
+  if (E <= 64) return nth_active_expert_t<1>(offsets, slot_of_expert, expert_addr, E, a);
+  if (E <= 128) return nth_active_expert_t<2>(offsets, slot_of_expert, expert_addr, E, a);
+  if (E <= 256) return nth_active_expert_t<4>(offsets, slot_of_expert, expert_addr, E, a);
+  if (E <= 512) return nth_active_expert_t<8>(offsets, slot_of_expert, expert_addr, E, a);
+  return nth_active_expert_t<16>(offsets, slot_of_expert, expert_addr, E, a);
 }
 
 }  // namespace moe

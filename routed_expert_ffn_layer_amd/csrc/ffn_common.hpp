@@ -37,10 +37,11 @@ __device__ __forceinline__ Item resolve_item_at(const FfnArgs& a, int b, int sha
   const int item = b / routed_tiles;
   it.tile = b - item * routed_tiles;
   it.shared = false;
-  const int e = uniform(nth_active_expert(a.offsets, a.slot_of_expert, a.E, item));
+  const int e = uniform(nth_active_expert(a.offsets, a.slot_of_expert, a.expert_addr, a.E, item));
   it.valid = e >= 0;
   if (!it.valid) return it;
-  it.w = uniform(a.slot_pool + (uint64_t)uniform(a.slot_of_expert[e]) * a.slot_stride);
+  it.w = a.expert_addr ? uniform(reinterpret_cast<const uint8_t*>(a.expert_addr[e]))
+                       : uniform(a.slot_pool + (uint64_t)uniform(a.slot_of_expert[e]) * a.slot_stride);
   it.I = a.I;
   it.p0 = uniform(a.offsets[e]);
   it.n = uniform(a.offsets[e + 1]) - it.p0;

@@ -121,11 +121,63 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
+// Router projection for batches of 32 tokens or more, as one bf16 MFMA GEMM
+// (v_mfma_f32_32x32x16_bf16): a wave computes a 32-expert x 32-token tile, the
+// router rows as the A operand (lane l: expert l % 32) and the tokens as B (lane
+// l: token l % 32); lane half l / 32 takes k = 8 (l / 32) .. +7 of every 16-wide
+// step for both operands, so A and B agree on the k order whatever it is inside
+// the instruction.  The K loop runs in order, so results are deterministic.
+// D: lane l, element v holds expert 8 (v / 4) + 4 (l / 32) + v % 4 of the tile,
+// token l % 32.  Tiles past E or T clamp their loads to the last row and are not
+// stored.  Grid (ceil(T / 32), ceil(E / 128)) of 4-wave blocks, wave w taking
+// expert tile 4 * blockIdx.y + w.  H must be a multiple of 16.
+constexpr int kRouterUnroll = 16;
+
+__global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wr, int T, int H, int E,
+                                                          float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63, hh = lane >> 5, j = lane & 31;
+  const int t0 = blockIdx.x * 32, e0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * 32;
+  if (e0 >= E) return;  // uniform per wave
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + (size_t)min(t0 + j, T - 1) * H) + hh;
+  const u32x4* wrow = reinterpret_cast<const u32x4*>(wr + (size_t)min(e0 + j, E - 1) * H) + hh;
+  const int steps = H / 16;
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  int s = 0;
+  for (; s + kRouterUnroll <= steps; s += kRouterUnroll) {
+    u32x4 a[kRouterUnroll], b[kRouterUnroll];
+#pragma unroll
+    for (int u = 0; u < kRouterUnroll; ++u) {
+      a[u] = wrow[2 * (s + u)];
+      b[u] = xr[2 * (s + u)];
+    }
+#pragma unroll
+    for (int u = 0; u < kRouterUnroll; ++u)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[u]), as_bf16x8(b[u]), acc, 0, 0, 0);
+  }
+  for (; s < steps; ++s)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wrow[2 * s]), as_bf16x8(xr[2 * s]), acc, 0, 0, 0);
+  if (t0 + j >= T) return;
+  float* out = logits + (size_t)(t0 + j) * E;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int e = e0 + 8 * (v / 4) + 4 * hh + (v % 4);
+    if (e < E) out[e] = acc[v];
+  }
+}
+
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E, float* logits,
                                 hipStream_t st) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((unsigned)T, (unsigned)((E + 4 * kRouterEPW - 1) / (4 * kRouterEPW))), block(256);
-  hipLaunchKernelGGL(router_logits_kernel, grid, block, 0, st, x, wr, H, E, logits);
+  if (T >= 32 && H % 16 == 0) {
+    const dim3 grid((unsigned)((T + 31) / 32), (unsigned)((E + 127) / 128)), block(256);
+    hipLaunchKernelGGL(router_logits_mfma, grid, block, 0, st, x, wr, T, H, E, logits);
+  } else {
+    const dim3 grid((unsigned)T, (unsigned)((E + 4 * kRouterEPW - 1) / (4 * kRouterEPW))), block(256);
+    hipLaunchKernelGGL(router_logits_kernel, grid, block, 0, st, x, wr, H, E, logits);
+  }
   return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@ class LayerBuffers:
         self.y = torch.empty((T, H), dtype=f32 if self.ydt == moe.MOE_F32 else torch.bfloat16, device=dev)
         self.slot_table = torch.empty(E, dtype=i32, device=dev)
         self.slot_misses = torch.empty(E, dtype=i32, device=dev)
+        self.addr_inplace = torch.empty(E, dtype=torch.int64, device=dev)
 
 
 def identity_slots(E, device="cuda"):
@@ -91,6 +92,35 @@ def forward_cached_split(b: LayerBuffers, cache: moe.MoeCache, layer, logits, x,
             ffn(b, x, slot_pool, slot_stride, b.slot_misses, None, stream)
         w += 1
         if w >= stats["n_waves"]:
+            break
+    combine(b, shared_w is not None, stream)
+    return b.y, waves
+
+
+def forward_cached_inplace(b: LayerBuffers, cache: moe.MoeCache, layer, logits, x, slot_pool, slot_stride,
+                           shared_w=None, stream=None):
+    """As forward_cached_split, with the cache's miss split: the step's in-place
+    experts are computed straight from their pinned host copies (read by the GPU
+    over the host link, no slot taken) right after the hits, while the filled
+    misses are still on their way; the three FFN calls write disjoint rows and the
+    combine adds them in the fixed order, so y equals the all-filled layer bit for
+    bit."""
+    route(b, logits, stream)
+    waves = []
+    w = 0
+    while True:
+        stats = cache.lookup_fill_inplace(layer, b.counts if w == 0 else None, w, b.slot_table, b.slot_misses,
+                                          b.addr_inplace, stream)
+        waves.append(stats)
+        ffn(b, x, slot_pool, slot_stride, b.slot_table, shared_w if w == 0 else None, stream)
+        if w == 0 and stats["inplace"]:
+            moe.moe_grouped_ffn_addr(b.wdt, b.addr_inplace, None, 0, x, b.offsets, b.sorted_rows, b.T, b.k, b.E,
+                                     b.H, b.I, b.out_rows, None, b.workspace, stream)
+        cache.wait_fills(stream)
+        if stats["fill_bytes"]:
+            ffn(b, x, slot_pool, slot_stride, b.slot_misses, None, stream)
+        w += 1
+        if w >= max(stats["n_waves"], 1):
             break
     combine(b, shared_w is not None, stream)
     return b.y, waves

@@ -33,7 +33,7 @@ class CacheDesc(ctypes.Structure):
 class CacheStats(ctypes.Structure):
     _fields_ = [("accesses", ctypes.c_int64), ("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
                 ("cold_misses", ctypes.c_int64), ("fill_bytes", ctypes.c_int64), ("n_waves", ctypes.c_int32),
-                ("wave_accesses", ctypes.c_int32)]
+                ("wave_accesses", ctypes.c_int32), ("inplace", ctypes.c_int64)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -53,7 +53,8 @@ class LayerStreamDesc(ctypes.Structure):
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_last_error", "moe_expert_bytes", "moe_route_topk",
            "moe_permute", "moe_cache_create", "moe_cache_destroy", "moe_cache_lookup_fill",
            "moe_cache_lookup_host", "moe_cache_state", "moe_cache_inject_fill_failure",
-           "moe_cache_lookup_fill_split", "moe_cache_wait_fills", "moe_route", "moe_cache_resize", "moe_route_project",
+           "moe_cache_lookup_fill_split", "moe_cache_wait_fills", "moe_cache_set_fill_fraction",
+           "moe_cache_lookup_fill_inplace", "moe_cache_step_inplace", "moe_grouped_ffn_addr", "moe_route", "moe_cache_resize", "moe_route_project",
            "moe_grouped_ffn_workspace", "moe_grouped_ffn_kind", "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down",
            "moe_combine", "moe_layer_stream_create", "moe_layer_stream_destroy", "moe_layer_stream_fill",
            "moe_layer_stream_acquire", "moe_layer_stream_release"]
@@ -84,6 +85,10 @@ def lib():
     L.moe_cache_lookup_host.argtypes = [P, i, P, i, P, P, i, ctypes.POINTER(i), ctypes.POINTER(CacheStats)]
     L.moe_cache_lookup_fill_split.argtypes = [P, i, P, i, P, P, ctypes.POINTER(CacheStats), P]
     L.moe_cache_wait_fills.argtypes = [P, P]
+    L.moe_cache_set_fill_fraction.argtypes = [P, i, i]
+    L.moe_cache_lookup_fill_inplace.argtypes = [P, i, P, i, P, P, P, ctypes.POINTER(CacheStats), P]
+    L.moe_cache_step_inplace.argtypes = [P, P, ctypes.POINTER(i)]
+    L.moe_grouped_ffn_addr.argtypes = [i, P, P, i, P, P, P, i, i, i, i, i, P, P, P, sz, P]
     L.moe_cache_resize.argtypes = [P, i, P, sz, P, P]
     L.moe_cache_state.argtypes = [P, P, P]
     L.moe_cache_inject_fill_failure.argtypes = [P, ctypes.c_int64]
@@ -191,6 +196,14 @@ def moe_grouped_ffn_down(wdt, slot_pool, slot_stride, slot_of_expert, shared_w, 
          sorted_rows, T, k, E, H, I, out_rows, shared_out, workspace, stream)
 
 
+def moe_grouped_ffn_addr(wdt, expert_addr, shared_w, I_shared, x, offsets, sorted_rows, T, k, E, H, I, out_rows,
+                         shared_out, workspace, stream=None):
+    _check(lib().moe_grouped_ffn_addr(wdt, _ptr(expert_addr), _ptr(shared_w), I_shared, _ptr(x), _ptr(offsets),
+                                      _ptr(sorted_rows), T, k, E, H, I, _ptr(out_rows), _ptr(shared_out),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
+
+
 def moe_combine(out_rows, topk_w, inv_rows, shared_out, y, ydt, stream=None):
     T, k = topk_w.shape
     H = y.shape[-1]
@@ -251,6 +264,23 @@ class MoeCache:
 
     def wait_fills(self, stream=None):
         _check(lib().moe_cache_wait_fills(self._h, _stream(stream)))
+
+    def set_fill_fraction(self, num, den):
+        _check(lib().moe_cache_set_fill_fraction(self._h, num, den))
+
+    def lookup_fill_inplace(self, layer, counts, wave, slot_hits, slot_misses, addr_inplace, stream=None):
+        st = CacheStats()
+        _check(lib().moe_cache_lookup_fill_inplace(self._h, layer, _ptr(counts), wave, _ptr(slot_hits),
+                                                   _ptr(slot_misses), _ptr(addr_inplace), ctypes.byref(st),
+                                                   _stream(stream)))
+        return st.as_dict()
+
+    def step_inplace(self):
+        import numpy as np
+        out = np.empty(self.n_experts, np.int32)
+        n = ctypes.c_int(0)
+        _check(lib().moe_cache_step_inplace(self._h, out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n)))
+        return out[:n.value].copy()
 
     def lookup_host(self, layer, counts_host, wave):
         """counts_host: numpy int32 [E] (ignored for wave > 0).  Returns (slot table, fills, stats)."""

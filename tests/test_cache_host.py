@@ -12,9 +12,12 @@ def _counts(ids, E):
     return np.bincount(np.asarray(ids).ravel(), minlength=E).astype(np.int32)
 
 
-def _step_both(lib_cache, ora_lru, layer, counts, E, S):
-    r = ora_lru.step(layer, counts)
+def _step_both(lib_cache, ora_lru, layer, counts, E, S, fill=None):
+    r = ora_lru.step(layer, counts, fill=fill)
     table, fills, st = lib_cache.lookup_host(layer, counts, 0)
+    np.testing.assert_array_equal(lib_cache.step_inplace(), r["inplace"])
+    assert st["inplace"] == len(r["inplace"])
+    assert st["misses"] == int((r["hit"] == 0).sum()) + len(r["inplace"])
     assert st["n_waves"] == r["n_waves"]
     waves = [(table, fills, st)]
     for w in range(1, r["n_waves"]):
@@ -26,9 +29,9 @@ def _step_both(lib_cache, ora_lru, layer, counts, E, S):
         np.testing.assert_array_equal(table, exp_table)
         miss = sel & (r["hit"] == 0)
         assert fills == [(int(s), layer, int(e), w) for e, s in zip(r["expert"][miss], r["slot"][miss])]
-        assert st["accesses"] == len(r["expert"])
+        assert st["accesses"] == len(r["expert"]) + len(r["inplace"])
         assert st["hits"] == int(r["hit"].sum())
-        assert st["cold_misses"] == int(((r["hit"] == 0) & (r["cold"] == 1)).sum())
+        assert st["cold_misses"] == int(((r["hit"] == 0) & (r["cold"] == 1)).sum()) + int(r["inplace_cold"].sum())
         assert st["wave_accesses"] == int(sel.sum())
     return r
 
@@ -210,3 +213,47 @@ def test_cached_trace_full_matches_oracle(ora):
     assert first_evict is not None and first_evict < n_tok // 2
     print(f"cached trace: {misses} misses of {accesses} accesses ({misses / accesses:.2%}), "
           f"first eviction at token {first_evict}")
+
+
+@pytest.mark.parametrize("fill", [(0, 1), (1, 2), (2, 3), (3, 4)])
+def test_miss_split_matches_oracle(ora, fill):
+    """The library's split of misses (filled / computed in place) against the
+    oracle's: same slots, fills, in-place experts and final state, on the
+    cached-trace recipe at reduced size and on random steps with several waves."""
+    cfg = synth.CONFIGS["cached_trace_bf16"]
+    E, L, k = cfg["E"], 6, cfg["k"]
+    S = int(0.37 * L * E)
+    lg = synth.trace_logits(cfg["seed"], 60, L, E, s=cfg["zipf_s"], reuse_p=cfg["reuse_p"])
+    c = moe.MoeCache(L, E, S)
+    c.set_fill_fraction(*fill)
+    o = ora.LRU(S, L, E)
+    n_inplace = 0
+    for t in range(60):
+        for l in range(L):
+            ids, _, _ = ora.route_topk(lg[t, l][None, :], k)
+            r = _step_both(c, o, l, _counts(ids, E), E, S, fill=fill)
+            n_inplace += len(r["inplace"])
+    _same_state(c, o)
+    assert n_inplace > 0
+    g = np.random.default_rng(3)
+    E2, S2 = 24, 5
+    c2 = moe.MoeCache(3, E2, S2)
+    c2.set_fill_fraction(*fill)
+    o2 = ora.LRU(S2, 3, E2)
+    for t in range(200):
+        layer = int(g.integers(0, 3))
+        _step_both(c2, o2, layer, _counts(g.choice(E2, size=int(g.integers(0, 12)), replace=False), E2), E2, S2,
+                   fill=fill)
+    _same_state(c2, o2)
+
+
+def test_fill_fraction_arguments():
+    c = moe.MoeCache(1, 8, 2)
+    for bad in ((-1, 2), (3, 2), (0, 0)):
+        with pytest.raises(moe.MoeError) as e:
+            c.set_fill_fraction(*bad)
+        assert e.value.status == moe.MOE_EINVAL
+    c.lookup_host(0, np.ones(8, np.int32), 0)      # a step of 4 waves left open
+    with pytest.raises(moe.MoeError) as e:
+        c.set_fill_fraction(1, 2)
+    assert e.value.status == moe.MOE_ESTATE

@@ -221,3 +221,50 @@ def test_device_resize_mid_trace(ora):
             lru.step(l, bc.counts.cpu().numpy())
             _same_state(cache, lru)
     cache.close()
+
+
+@pytest.mark.parametrize("fill", [(1, 2), (0, 1), (2, 3)], ids=["half", "none", "two_thirds"])
+def test_miss_split_bitwise_equal_to_resident(ora, fill):
+    """The miss split: of each step's misses the first floor(m num/den + 1/2) are
+    filled, the rest computed in place by the FFN reading their pinned host copies
+    directly.  Every layer equals the all-resident layer bit for bit (the in-place
+    rows merge through the same fixed-order combine), and the cache state equals
+    the oracle's LRU with the same split after every step.  A shared expert and
+    T = 3 tokens per step (several misses per step), bf16 experts."""
+    H, I, E, k, Ls, tokens, T = 256, 128, 64, 8, 6, 16, 3
+    S = int(0.37 * Ls * E)
+    seed = 1105
+    lg = synth.trace_logits(seed, tokens * T, Ls, E, s=1.0, reuse_p=0.7)
+    experts = np.stack([synth.random_expert(synth.BF16, H, I, synth.rng(seed, 3, l, e)) for l in range(Ls)
+                        for e in range(E)])
+    shared = synth.random_expert(synth.BF16, H, 128, synth.rng(seed, 4))
+    eb = experts.shape[1]
+    host = _pinned_pool(experts)
+    cache, slot_pool, stride = _device_cache(Ls, E, S, eb, host)
+    cache.set_fill_fraction(*fill)
+    lru = ora.LRU(S, Ls, E)
+    resident = to_dev(experts)
+    sh = to_dev(shared)
+    b = L.LayerBuffers(T, E, k, H, I, synth.BF16, I_shared=128)
+    bc = L.LayerBuffers(T, E, k, H, I, synth.BF16, I_shared=128)
+    n_inplace = n_fills = 0
+    for t in range(tokens):
+        x = to_dev(synth.encode_activations(synth.BF16, synth.normal_x(seed, T, H, t)))
+        for l in range(Ls):
+            lg_d = to_dev(np.ascontiguousarray(lg[t * T:(t + 1) * T, l]))
+            L.forward(b, lg_d, x, resident[l * E:(l + 1) * E], eb, L.identity_slots(E), sh)
+            torch.cuda.synchronize()
+            y_ref = b.y.clone()
+            y, waves = L.forward_cached_inplace(bc, cache, l, lg_d, x, slot_pool, stride, sh)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), (t, l)
+            r = lru.step(l, bc.counts.cpu().numpy(), fill=fill)
+            assert waves[0]["inplace"] == len(r["inplace"])
+            assert waves[0]["misses"] == int((r["hit"] == 0).sum()) + len(r["inplace"])
+            n_inplace += waves[0]["inplace"]
+            n_fills += int((r["hit"] == 0).sum())
+            _same_state(cache, lru)
+    log(f"miss split {fill}: {n_fills} fills, {n_inplace} computed in place")
+    assert n_inplace > 0
+    assert (n_fills == 0) == (fill == (0, 1))
+    cache.close()
