@@ -297,6 +297,22 @@ int moe_grouped_ffn_addr(int wdt, const uint64_t* expert_addr, const void* share
                          const int32_t* offsets, const int32_t* sorted_rows, int T, int k, int E, int H, int I,
                          float* out_rows, float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* moe_grouped_ffn for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops or harnesses that forbid hipMalloc): the same
+ * arguments and results without the workspace.  The SwiGLU intermediate goes to a
+ * fixed array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends; its device address is looked up on the first
+ * call on each device (with that device current).  The call allocates nothing.
+ * MOE_ECAPACITY if moe_grouped_ffn_workspace() for the shape exceeds the array
+ * (32 MiB: e.g. up to 8192 token-expert pairs at I = 2048).  Every call on one GPU
+ * uses the same array, so calls that overlap on one GPU (several streams or
+ * threads) race; nothing in it needs clearing between calls. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int moe_grouped_ffn_noalloc(int wdt, const void* slot_pool, size_t slot_stride, const int32_t* slot_of_expert,
+                            const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
+                            const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
+                            float* shared_out, hipStream_t stream);
+
 /* Which kernel family moe_grouped_ffn runs for a shape (the results are the same
  * computation either way): MOE_FFN_WEIGHT_STREAM (decode-sized batches: each
  * expert's weights stream once past its few tokens) or MOE_FFN_GROUPED_GEMM

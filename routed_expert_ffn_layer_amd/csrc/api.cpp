@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -298,6 +299,64 @@ int moe_grouped_ffn_down(int wdt, const void* slot_pool, size_t slot_stride, con
                          float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
   return grouped_ffn(PHASE_DOWN, wdt, slot_pool, slot_stride, slot_of_expert, shared_w, I_shared, x, offsets,
                      sorted_rows, T, k, E, H, I, out_rows, shared_out, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free grouped FFN.  The SwiGLU intermediate goes to a fixed device
+// array instead of a caller workspace.  Every GPU the library runs on holds its
+// own copy of the array (MOE_NOALLOC_SCRATCH_BYTES) until the process ends; its
+// address on a device is looked up once, with that device current, and kept.  In
+// host code `scratch` names a host-side stand-in, never the device memory: only
+// the looked-up pointer is handed to kernels.
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_EUNSUPPORTED, "moe_grouped_ffn_noalloc: device %d beyond the %d this build tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn_noalloc: hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MOE_EHIP, "moe_grouped_ffn_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_grouped_ffn_noalloc(int wdt, const void* slot_pool, size_t slot_stride, const int32_t* slot_of_expert,
+                            const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
+                            const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
+                            float* shared_out, hipStream_t stream) {
+  if (int rc = check_routing(T, E, k)) return rc;
+  if (int rc = check_dims(wdt, H, I, "moe_grouped_ffn_noalloc")) return rc;
+  if (I_shared < 0) return fail(MOE_EINVAL, "moe_grouped_ffn_noalloc: I_shared=%d < 0", I_shared);
+  const size_t need = moe::ffn_workspace_bytes(wdt, T, k, I, shared_w ? I_shared : 0);
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ECAPACITY, "moe_grouped_ffn_noalloc: the intermediate needs %zu bytes, more than the %zu of "
+                "the fixed scratch array", need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (int rc = scratch_of_current_device(&ws)) return rc;
+  return grouped_ffn(PHASE_GATE_UP | PHASE_DOWN, wdt, slot_pool, slot_stride, slot_of_expert, shared_w, I_shared, x,
+                     offsets, sorted_rows, T, k, E, H, I, out_rows, shared_out, ws, MOE_NOALLOC_SCRATCH_BYTES,
+                     stream);
 }
 
 }  // extern "C"

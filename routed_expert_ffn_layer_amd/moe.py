@@ -55,7 +55,7 @@ EXPORTS = ["moe_abi_version", "moe_status_str", "moe_last_error", "moe_expert_by
            "moe_cache_lookup_host", "moe_cache_state", "moe_cache_inject_fill_failure",
            "moe_cache_lookup_fill_split", "moe_cache_wait_fills", "moe_cache_set_fill_fraction",
            "moe_cache_lookup_fill_inplace", "moe_cache_step_inplace", "moe_grouped_ffn_addr", "moe_route", "moe_cache_resize", "moe_route_project",
-           "moe_grouped_ffn_workspace", "moe_grouped_ffn_kind", "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down",
+           "moe_grouped_ffn_workspace", "moe_grouped_ffn_kind", "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down", "moe_grouped_ffn_noalloc",
            "moe_combine", "moe_layer_stream_create", "moe_layer_stream_destroy", "moe_layer_stream_fill",
            "moe_layer_stream_acquire", "moe_layer_stream_release"]
 
@@ -99,6 +99,7 @@ def lib():
     L.moe_grouped_ffn.argtypes = ffn_args
     L.moe_grouped_ffn_gate_up.argtypes = ffn_args
     L.moe_grouped_ffn_down.argtypes = ffn_args
+    L.moe_grouped_ffn_noalloc.argtypes = [i, P, sz, P, P, i, P, P, P, i, i, i, i, i, P, P, P]
     L.moe_combine.argtypes = [P, P, P, P, i, i, i, P, i, P]
     L.moe_layer_stream_create.argtypes = [ctypes.POINTER(LayerStreamDesc), ctypes.POINTER(P)]
     L.moe_layer_stream_destroy.argtypes = [P]
@@ -202,6 +203,16 @@ def moe_grouped_ffn_addr(wdt, expert_addr, shared_w, I_shared, x, offsets, sorte
                                       _ptr(sorted_rows), T, k, E, H, I, _ptr(out_rows), _ptr(shared_out),
                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def moe_grouped_ffn_noalloc(wdt, slot_pool, slot_stride, slot_of_expert, shared_w, I_shared, x, offsets, sorted_rows,
+                            T, k, E, H, I, out_rows, shared_out, stream=None):
+    _check(lib().moe_grouped_ffn_noalloc(wdt, _ptr(slot_pool), slot_stride, _ptr(slot_of_expert), _ptr(shared_w),
+                                         I_shared, _ptr(x), _ptr(offsets), _ptr(sorted_rows), T, k, E, H, I,
+                                         _ptr(out_rows), _ptr(shared_out), _stream(stream)))
 
 
 def moe_combine(out_rows, topk_w, inv_rows, shared_out, y, ydt, stream=None):
