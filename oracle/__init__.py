@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 SOURCES = [os.path.join(HERE, "moe_oracle.c")]
 
-F32, BF16, MXFP4 = 0, 1, 2
+F32, BF16, MXFP4, MXFP4_A8 = 0, 1, 2, 3
 
 _lib = None
 
@@ -43,6 +43,9 @@ def lib():
         L.ora_e2m1_value.argtypes = [ctypes.c_uint8]
         L.ora_e8m0_value.restype = ctypes.c_double
         L.ora_e8m0_value.argtypes = [ctypes.c_uint8]
+        L.ora_e4m3_value.restype = ctypes.c_double
+        L.ora_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.ora_mx8_quantize.argtypes = [P, i, i, P, P]
         L.ora_expert_bytes.restype = ctypes.c_size_t
         L.ora_expert_bytes.argtypes = [i, i, i]
         L.ora_decode_expert.argtypes = [i, P, i, i, P, P, P]
@@ -90,6 +93,20 @@ def bf16_value(bits: int) -> float:
 
 def e2m1_value(code: int) -> float:
     return lib().ora_e2m1_value(int(code))
+
+
+def e4m3_value(code: int) -> float:
+    return float(lib().ora_e4m3_value(code))
+
+
+def mx8_quantize(x_bits):
+    """bf16 bits [T][H] -> (E4M3 codes uint8 [T][H], E8M0 scales uint8 [T][H/32])."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, H = x.shape
+    codes = np.empty((T, H), np.uint8)
+    scales = np.empty((T, H // 32), np.uint8)
+    _check(lib().ora_mx8_quantize(_p(x), T, H, _p(codes), _p(scales)), "mx8_quantize")
+    return codes, scales
 
 
 def e8m0_value(code: int) -> float:

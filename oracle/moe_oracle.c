@@ -45,6 +45,55 @@ double ora_e8m0_value(uint8_t code) {
   return ldexp(1.0, (int)code - 127);
 }
 
+/* E4M3 element of OCP MX v1.0 (the activations of the native FP4 path): bit 7 the
+ * sign, bits 6..3 the exponent (bias 7), bits 2..0 the mantissa; exponent field 0
+ * holds the subnormals m/8 * 2^-6; S.1111.111 is NaN (no infinities). */
+double ora_e4m3_value(uint8_t code) {
+  const int e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+  return (code & 0x80u) ? -v : v;
+}
+
+/* MXFP8 quantization, written out: block scale from the block's largest
+ * magnitude, then each scaled element to the nearest finite E4M3 value found by
+ * trying every code (ties to the even code; anything beyond 448 lands on 448). */
+int ora_mx8_quantize(const uint16_t* x, int T, int H, uint8_t* codes, uint8_t* scales) {
+  if (T < 0 || H <= 0 || H % 32) return -1;
+  for (int t = 0; t < T; ++t)
+    for (int b = 0; b < H / 32; ++b) {
+      const uint16_t* xb = x + (size_t)t * H + (size_t)b * 32;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) {
+        const double a = fabs(ora_bf16_value(xb[i]));
+        if (a > amax) amax = a;
+      }
+      int X = -127;
+      if (amax > 0.0) {
+        int e2;
+        frexp(amax, &e2);  /* amax = f * 2^e2, f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+        X = e2 - 1 - 8;
+        if (X < -127) X = -127;
+        if (X > 127) X = 127;
+      }
+      scales[(size_t)t * (H / 32) + b] = (uint8_t)(X + 127);
+      for (int i = 0; i < 32; ++i) {
+        const double v = ldexp(ora_bf16_value(xb[i]), -X), a = fabs(v);
+        int best = 0;
+        double best_d = INFINITY;
+        for (int c = 0; c <= 0x7E; ++c) {
+          const double d = fabs(ora_e4m3_value((uint8_t)c) - a);
+          if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+          }
+        }
+        codes[(size_t)t * H + (size_t)b * 32 + i] = (uint8_t)(best | (signbit(v) ? 0x80 : 0));
+      }
+    }
+  return 0;
+}
+
 /* Tiled slot layout (a reading: the pages say only that experts are stored in
  * pinned host memory in the layout they are computed from, "Three mechanisms",
  * elastic memory management).
@@ -110,6 +159,7 @@ static size_t scale_bytes(int rows, int K) {
 
 size_t ora_expert_bytes(int dtype, int H, int I) {
   if (H <= 0 || I <= 0) return 0;
+  if (dtype == ORA_MXFP4_A8) dtype = ORA_MXFP4;  /* same weights */
   if (dtype == ORA_F32 || dtype == ORA_BF16) return matrix_bytes(dtype, 2 * I, H) + matrix_bytes(dtype, H, I);
   if (dtype != ORA_MXFP4 || H % 32 || I % 32) return 0;
   return matrix_bytes(dtype, 2 * I, H) + matrix_bytes(dtype, H, I) + scale_bytes(2 * I, H) + scale_bytes(H, I);
@@ -124,6 +174,7 @@ size_t ora_expert_bytes(int dtype, int H, int I) {
 int ora_decode_expert(int dtype, const uint8_t* slot, int H, int I, double* wg, double* wu, double* wd) {
   const uint8_t *w13, *w2, *s13 = NULL, *s2 = NULL;
   if (H <= 0 || I <= 0) return -1;
+  if (dtype == ORA_MXFP4_A8) dtype = ORA_MXFP4;  /* same weights */
   if (dtype == ORA_F32) {
     w13 = slot;
     w2 = slot + matrix_bytes(dtype, 2 * I, H);
@@ -162,6 +213,14 @@ int ora_decode_x(int dtype, const void* x, int T, int H, double* out) {
   } else if (dtype == ORA_BF16 || dtype == ORA_MXFP4) {
     const uint16_t* b = (const uint16_t*)x;
     for (size_t i = 0; i < n; ++i) out[i] = ora_bf16_value(b[i]);
+  } else if (dtype == ORA_MXFP4_A8) {
+    if (H % 32) return -1;
+    uint8_t* codes = (uint8_t*)malloc(n ? n : 1);
+    uint8_t* scales = (uint8_t*)malloc(n / 32 + 1);
+    if (!codes || !scales) { free(codes); free(scales); return -3; }
+    ora_mx8_quantize((const uint16_t*)x, T, H, codes, scales);
+    for (size_t i = 0; i < n; ++i) out[i] = ora_e4m3_value(codes[i]) * ora_e8m0_value(scales[i / 32]);
+    free(codes); free(scales);
   } else {
     return -1;
   }

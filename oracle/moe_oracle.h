@@ -25,15 +25,27 @@ extern "C" {
 #define ORA_F32 0
 #define ORA_BF16 1
 #define ORA_MXFP4 2
+/* MXFP4 weights with the gate/up activations quantized to MXFP8 (E4M3 elements,
+ * one E8M0 scale per 32 consecutive elements of a token row), OCP MX v1.0. */
+#define ORA_MXFP4_A8 3
 
 /* ---- stored formats -> exact fp64 ---------------------------------------- */
 double ora_bf16_value(uint16_t bits);
 double ora_e2m1_value(uint8_t code);   /* low 4 bits used */
 double ora_e8m0_value(uint8_t code);   /* 0xFF is NaN */
+double ora_e4m3_value(uint8_t code);   /* 0x7F and 0xFF are NaN */
+/* MXFP8 (E4M3) quantization of bf16 activations x [T][H] (H a multiple of 32), OCP
+ * MX v1.0: per block of 32 elements along a row the shared exponent is
+ * X = floor(log2(max |x|)) - 8 (8 = the largest E4M3 exponent), clamped to
+ * [-127, 127] (X = -127 for an all-zero block); scales [T][H/32] = X + 127; each
+ * element x / 2^X becomes the nearest finite E4M3 value, ties to the even code,
+ * magnitudes beyond 448 clamped to 448. codes [T][H]. */
+int ora_mx8_quantize(const uint16_t* x, int T, int H, uint8_t* codes, uint8_t* scales);
 size_t ora_expert_bytes(int dtype, int H, int I);
 /* Decode one expert slot into fp64 Wg [I][H], Wu [I][H], Wd [H][I]. */
 int ora_decode_expert(int dtype, const uint8_t* slot, int H, int I, double* wg, double* wu, double* wd);
-/* Decode activations: f32 [T][H] for ORA_F32, bf16 bits [T][H] otherwise. */
+/* Decode activations: f32 [T][H] for ORA_F32, bf16 bits [T][H] otherwise; for
+ * ORA_MXFP4_A8 the bf16 values after their MXFP8 quantization (ora_mx8_quantize). */
 int ora_decode_x(int dtype, const void* x, int T, int H, double* out);
 
 /* ---- routing -------------------------------------------------------------- */

@@ -191,3 +191,87 @@ def test_mxfp4_roundtrip_of_representable_values(ora):
     np.testing.assert_array_equal(dg, wg)
     np.testing.assert_array_equal(du, wu)
     np.testing.assert_array_equal(dd, wd)
+
+
+# ---- MXFP8 (E4M3) activations of the native FP4 path (OCP MX v1.0) -------------
+
+def _e4m3_formula(v):
+    """E4M3 code of v by the closed-form rounding (not the oracle's search): RNE in
+    the subnormal steps of 2^-9 below 2^-6, else RNE of the 3-bit mantissa at
+    v's own exponent; beyond 448 the largest finite value."""
+    import math
+    sign = 0x80 if math.copysign(1.0, v) < 0 else 0
+    a = abs(v)
+    if a < 2.0 ** -6:
+        return sign | int(round(a * 512))          # Python round(): ties to even
+    _, e2 = math.frexp(a)
+    e = e2 - 1
+    m = int(round(math.ldexp(a, 3 - e)))           # 8 .. 16
+    if m == 16:
+        e, m = e + 1, 8
+    if e > 8 or (e == 8 and m > 14):
+        return sign | 0x7E
+    return sign | ((e + 7) << 3) | (m - 8)
+
+
+def test_e4m3_values_from_the_spec(ora):
+    import math
+    assert ora.e4m3_value(0x7E) == 448.0               # largest finite
+    assert ora.e4m3_value(0x08) == 2.0 ** -6           # smallest normal
+    assert ora.e4m3_value(0x01) == 2.0 ** -9           # smallest subnormal
+    assert ora.e4m3_value(0x38) == 1.0 and ora.e4m3_value(0x39) == 1.125 and ora.e4m3_value(0x36) == 0.875
+    assert math.isnan(ora.e4m3_value(0x7F)) and math.isnan(ora.e4m3_value(0xFF))
+    vals = [ora.e4m3_value(c) for c in range(0x7F)]
+    assert all(b > a for a, b in zip(vals, vals[1:])) and vals[0] == 0.0
+    assert all(ora.e4m3_value(c | 0x80) == -ora.e4m3_value(c) for c in range(1, 0x7F))
+
+
+def test_mx8_quantize_against_closed_form_rounding(ora):
+    import math
+    g = np.random.default_rng(8)
+    blocks = [g.standard_normal(32) * s for s in (1.0, 1e-3, 37.0, 3e-30)]
+    # crafted: exact halfway points (ties), the saturation band of the top element,
+    # zeros and -0, subnormal steps
+    b = np.full(32, 0.0)
+    b[0] = 1.0                                           # X = -8: elements scale by 256
+    b[1:9] = [(1 + 1 / 16) / 256, (1 + 3 / 16) / 256, (1 + 5 / 16) / 256, 2 ** -9 * 1.5 / 256,
+              2 ** -9 * 2.5 / 256, -(1 + 1 / 16) / 256, -0.0, 0.0]
+    blocks.append(b)
+    sat = np.full(32, 0.25)
+    sat[0] = 1.99                                        # scaled to ~509.4: clamps to 448
+    blocks.append(sat)
+    blocks.append(np.zeros(32))
+    x = synth.bf16_bits(np.concatenate(blocks).astype(np.float32)).reshape(len(blocks), 32)
+    codes, scales = ora.mx8_quantize(x)
+    for r in range(x.shape[0]):
+        v = synth.bf16_bits_to_f32(x[r]).astype(np.float64)
+        amax = np.abs(v).max()
+        X = -127 if amax == 0 else max(-127, math.frexp(amax)[1] - 1 - 8)
+        assert scales[r, 0] == X + 127
+        for i in range(32):
+            assert codes[r, i] == _e4m3_formula(math.ldexp(v[i], -X)), (r, i, v[i])
+    assert scales[4, 0] == 127 - 8 and codes[4, 7] == 0x80 and codes[4, 8] == 0x00
+    # ties go to the even code: 1.0625 -> 1.0, 1.1875 -> 1.25, 1.5 and 2.5 subnormal steps -> 2
+    assert list(codes[4, 1:6]) == [0x38, 0x3A, 0x3A, 0x02, 0x02] and codes[4, 6] == 0xB8
+    assert codes[5, 0] == 0x7E and scales[6, 0] == 0
+
+
+def test_mx8_quantize_is_identity_on_representable_values(ora):
+    """Values already of the form E4M3 x 2^X (block maximum fixing X) come back
+    unchanged, so an A8 layer on such activations equals the MXFP4 layer exactly."""
+    g = np.random.default_rng(9)
+    T, H = 3, 128
+    codes = g.integers(0, 0x7F, size=(T, H)).astype(np.uint8) | (g.integers(0, 2, size=(T, H)) * 0x80).astype(np.uint8)
+    codes[:, ::32] = 0x7E                                  # block maximum 448 -> X fixed by the exponent below
+    X = g.integers(-20, 20, size=(T, H // 32))
+    vals = np.array([[ora.e4m3_value(int(c)) for c in row] for row in codes]) * np.repeat(2.0 ** X, 32, axis=1)
+    x = synth.bf16_bits(vals.astype(np.float32))
+    assert np.array_equal(synth.bf16_bits_to_f32(x).astype(np.float64), vals)   # representable in bf16 too
+    q, s = ora.mx8_quantize(x)
+    np.testing.assert_array_equal(q, codes)
+    np.testing.assert_array_equal(s.astype(int), X + 127)
+    H2, I, E, k = 128, 64, 4, 2
+    lay = synth.small_layer(synth.MXFP4, T, H2, I, E, k, seed=3)
+    a = ora.layer(synth.MXFP4, lay["experts"], x, lay["logits"], k, H2, I)
+    b = ora.layer(ora.MXFP4_A8, lay["experts"], x, lay["logits"], k, H2, I)
+    np.testing.assert_array_equal(a["y"], b["y"])
