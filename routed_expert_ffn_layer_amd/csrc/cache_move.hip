@@ -24,13 +24,7 @@ struct MoveBatch {
   int32_t to[kMoveBatch];    // new slot of each move
 };
 
-#ifndef MOE_MOVE_WORDS
-#define MOE_MOVE_WORDS 1
-#endif
-#ifndef MOE_MOVE_NT
-#define MOE_MOVE_NT 1
-#endif
-constexpr int kMoveThreads = 256, kMoveWordsPerThread = MOE_MOVE_WORDS;  // per block: 4 KB x words
+constexpr int kMoveThreads = 256, kMoveWordsPerThread = 1;  // per block: 4 KB x words
 constexpr uint64_t kMoveBlockBytes = (uint64_t)kMoveThreads * kMoveWordsPerThread * 16;
 
 __global__ __launch_bounds__(kMoveThreads) void move_slots_kernel(MoveBatch m) {
@@ -44,17 +38,12 @@ __global__ __launch_bounds__(kMoveThreads) void move_slots_kernel(MoveBatch m) {
 #pragma unroll
   for (int j = 0; j < kMoveWordsPerThread; ++j) {
     const uint64_t w = w0 + (uint64_t)j * kMoveThreads;
-    if (w < words) v[j] = MOE_MOVE_NT ? __builtin_nontemporal_load(src + w) : src[w];
+    if (w < words) v[j] = __builtin_nontemporal_load(src + w);
   }
 #pragma unroll
   for (int j = 0; j < kMoveWordsPerThread; ++j) {
     const uint64_t w = w0 + (uint64_t)j * kMoveThreads;
-    if (w < words) {
-      if (MOE_MOVE_NT)
-        __builtin_nontemporal_store(v[j], dst + w);
-      else
-        dst[w] = v[j];
-    }
+    if (w < words) __builtin_nontemporal_store(v[j], dst + w);
   }
 }
 
