@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # dense; the scaled FP4 x FP8 MFMA runs at the FP8 rate
 METRIC = "MoE-layer tokens/s at 1 MI355X; % HBM BW (decode), % MFMA peak (prefill)"
 # HBM byte counters of each workload's dominant kernel (rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs summarised by --summarize-counters), valid while the FFN
@@ -53,7 +54,7 @@ COUNTERS = {
 }
 FFN_SOURCES = [os.path.join(ROOT, "routed_expert_ffn_layer_amd", "csrc", f)
                for f in ("ffn.hip", "ffn_prefill.hip", "ffn_common.hpp", "common.hpp")]
-WORKLOADS = ("decode_bf16", "decode_mxfp4", "prefill_mxfp4", "cached_trace_bf16", "hostbw")
+WORKLOADS = ("decode_bf16", "decode_mxfp4", "prefill_mxfp4", "prefill_mxfp4_a8", "cached_trace_bf16", "hostbw")
 
 
 def parse():
@@ -735,13 +736,15 @@ def workload_hostbw(args):
 # ---------------------------------------------------------------------------
 # prefill_mxfp4: double-buffered layer streaming around 4096-token layers.
 
-def workload_prefill_mxfp4(args):
+def workload_prefill_mxfp4(args, native=False):
     import torch
     import synth
     from routed_expert_ffn_layer_amd import layer as L
     from routed_expert_ffn_layer_amd import moe
     c = synth.CONFIGS["prefill_mxfp4"]
-    H, I, E, k, T = c["H"], c["I"], c["E"], c["k"], args.tokens or c["T"]
+    H, I, E, k = c["H"], c["I"], c["E"], c["k"]
+    T = args.tokens or (8192 if native else c["T"])
+    wdt = moe.MOE_MXFP4_A8 if native else moe.MOE_MXFP4
     n_layers = args.layers or c["layers"]
     n_host = args.host_layers or 2
     steps, warmup = args.steps or 2, 1 if args.warmup is None else args.warmup
@@ -759,7 +762,7 @@ def workload_prefill_mxfp4(args):
     ptrs = (ctypes.c_void_p * n_layers)(*[host[l % n_host].data_ptr() for l in range(n_layers)])
     fill_stream = torch.cuda.Stream()
     ls = moe.LayerStream(n_layers, lb, banks[0], banks[1], fill_stream, host_layer_ptrs=ptrs)
-    b = L.LayerBuffers(T, E, k, H, I, moe.MOE_MXFP4)
+    b = L.LayerBuffers(T, E, k, H, I, wdt)
     n_x = 4
     logits = [torch.from_numpy(synth.normal_logits(c["seed"], T, E, 7, l)).to(dev) for l in range(n_layers)]
     xs = [torch.from_numpy(synth.encode_activations(synth.BF16, synth.normal_x(c["seed"], T, H, 7, j))
@@ -824,18 +827,22 @@ def workload_prefill_mxfp4(args):
     bp = host_to_device_gbs(lb, reps=3)
     ls.close()
     cpu = None if args.no_cpu_baseline else cpu_prefill_mxfp4(banks[0], logits[0], xs[0], c, T, args.cpu_seconds,
-                                                              *cpu_threads(args))
+                                                              *cpu_threads(args), dtype=wdt)
     gu_tf = gu_flop / gu / 1e12
+    peak = MFMA_FP8_PEAK_TFLOPS if native else MFMA_BF16_PEAK_TFLOPS
     line = out_line(
-        T * n_layers / t_pipe, "layer-tokens/s", steps, warmup, t_pipe * 1e3, "bf16 (MXFP4 weights)",
+        T * n_layers / t_pipe, "layer-tokens/s", steps, warmup, t_pipe * 1e3,
+        "fp4 x fp8 (MXFP4 weights, MXFP8 gate/up activations)" if native else "bf16 (MXFP4 weights)",
         f"synthetic (seeded N(0,0.02) weights quantized to MXFP4, {n_host} distinct pinned host layers streamed "
         "as layer l mod that; N(0,1) logits and activations)",
-        {"workload": "prefill layer MXFP4: hidden 4096, 256 routed experts, top-6, intermediate 2048",
+        {"workload": ("prefill layer MXFP4 weights with MXFP8 gate/up activations (native FP4 MFMA): "
+                      if native else "prefill layer MXFP4: ") + "hidden 4096, 256 routed experts, top-6, intermediate 2048",
          "tokens_per_layer": T, "stacked_layers": n_layers, "host_layers_distinct": n_host,
          "layer_bytes": lb, "slots": "two HBM banks, one layer each"},
-        {"kernel": "prefill_gate_up<mxfp4> (moe_grouped_ffn_gate_up)", "bound": "mfma", "achieved": gu_tf,
-         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": gu_tf / MFMA_BF16_PEAK_TFLOPS,
-         "traffic": measured_traffic("prefill_mxfp4"),
+        {"kernel": ("mx8_quantize + grouped_gate_up<native fp4 x fp8>" if native else
+                    "grouped_gate_up<mxfp4> (moe_grouped_ffn_gate_up)"), "bound": "mfma", "achieved": gu_tf,
+         "peak": peak, "unit": "TFLOP/s", "frac": gu_tf / peak,
+         "traffic": None if native else measured_traffic("prefill_mxfp4"),
          "avg_launch_us": gu * 1e6, "algorithmic_flop_per_launch": gu_flop, "launches_timed": 10,
          "timing": "events around back-to-back gate_up launches on one layer's routing"},
         cpu,
@@ -845,9 +852,9 @@ def workload_prefill_mxfp4(args):
                   "fill_gbs": lb * n_layers / t_fill / 1e9, "host_to_device_gbs": bp},
         grouped_gemm={"gate_up_us": gu * 1e6, "down_us": dn * 1e6,
                       "tflops": layer_flop / (gu + dn) / 1e12,
-                      "mfma_frac": layer_flop / (gu + dn) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                      "mfma_frac_bf16_peak": layer_flop / (gu + dn) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                       "layer_tflops": layer_flop / (t_gemm / n_layers) / 1e12})
-    if not args.no_decode_leg:
+    if not args.no_decode_leg and not native:
         del banks, host, b, xs, logits
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
@@ -868,7 +875,7 @@ def decode_leg(args):
                                     "roofline", "layer_hbm_frac", "by_batch", "cpu_baseline") if key in d}
 
 
-def cpu_prefill_mxfp4(bank, logits_d, x_d, c, T, seconds, threads, model):
+def cpu_prefill_mxfp4(bank, logits_d, x_d, c, T, seconds, threads, model, dtype=2):
     """The oracle on a bounded sample of one prefill layer, on one thread and on
     `threads` threads: routing of all T tokens, then whole experts (each with all
     of its tokens, ascending expert id) until the budget is spent; the layer time
@@ -885,7 +892,7 @@ def cpu_prefill_mxfp4(bank, logits_d, x_d, c, T, seconds, threads, model):
     weights = {e: bank[e].cpu().numpy() for e, _ in jobs}  # copied to the host before the timed calls
 
     def work(e, tok):
-        return oracle.expert_rows(synth.MXFP4, weights[e], H, I, x, tok)
+        return oracle.expert_rows(dtype, weights[e], H, I, x, tok)
 
     legs = {}
     for n in (1, threads):
@@ -1062,7 +1069,9 @@ def main():
         calibrate_copy()
         return
     fn = {"decode_bf16": workload_decode_bf16, "decode_mxfp4": workload_decode_mxfp4,
-          "prefill_mxfp4": workload_prefill_mxfp4, "cached_trace_bf16": workload_cached_trace_bf16,
+          "prefill_mxfp4": workload_prefill_mxfp4,
+          "prefill_mxfp4_a8": lambda a: workload_prefill_mxfp4(a, native=True),
+          "cached_trace_bf16": workload_cached_trace_bf16,
           "hostbw": workload_hostbw}[args.workload]
     print(json.dumps(fn(args)), flush=True)
 

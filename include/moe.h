@@ -71,7 +71,14 @@ typedef enum {
   MOE_ESTATE = 6          /* call out of order (e.g. wave w before wave w-1) */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
+/* MOE_MXFP4_A8: MXFP4 weights (the MOE_MXFP4 slot layout) with the gate/up
+ * activations quantized to MXFP8 (OCP MX v1.0: E4M3 elements, one E8M0 scale per
+ * 32 consecutive elements of a token row, X = floor(log2 max|x|) - 8, round to
+ * nearest even, clamp to 448) and multiplied on the scaled FP4 x FP8 MFMA; the
+ * down projection stays on the exact path (bf16 intermediate).  A precision
+ * trade for prefill throughput (the pages' 8,192-token prefill chunks, "Data Check"
+ * claim table, Fig 4a row); the other types never lower activation precision. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2, MOE_MXFP4_A8 = 3 } moe_dtype;
 
 int moe_abi_version(void);
 const char* moe_status_str(int status);
@@ -281,7 +288,9 @@ int moe_cache_inject_fill_failure(moe_cache* c, int64_t n);
  *   workspace   >= moe_grouped_ffn_workspace() bytes of device memory
  * Arithmetic: f32 weights use f32 FMA; bf16 and MXFP4 weights use bf16 MFMA
  * with f32 accumulation (MXFP4 is expanded to bf16 exactly), and the SwiGLU
- * intermediate is rounded to bf16. */
+ * intermediate is rounded to bf16.  MOE_MXFP4_A8: gate/up multiply the E2M1
+ * weights by the MXFP8 activations exactly (f32 accumulation), H, I and
+ * I_shared multiples of 128 (MOE_EUNSUPPORTED otherwise). */
 size_t moe_grouped_ffn_workspace(int T, int k, int E, int H, int I, int I_shared, int wdt);
 int moe_grouped_ffn(int wdt, const void* slot_pool, size_t slot_stride, const int32_t* slot_of_expert,
                     const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
@@ -313,11 +322,21 @@ int moe_grouped_ffn_noalloc(int wdt, const void* slot_pool, size_t slot_stride, 
                             const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
                             float* shared_out, hipStream_t stream);
 
+/* MXFP8 quantization of activations, as MOE_MXFP4_A8 applies it before gate/up
+ * (OCP Microscaling Formats v1.0, the format of the pages' MXFP4 build, "Results"):
+ * x [T][H] bf16 (H a multiple of 32) -> codes [T][H] E4M3 bytes and scales
+ * [T][H/32] E8M0 bytes; per 32-element block of a row X = floor(log2 max|x|) - 8
+ * (X = -127 for an all-zero block), scale X + 127, each element x / 2^X rounded to
+ * the nearest E4M3 value, ties to even, clamped to +-448.  Deterministic: the codes
+ * depend on x alone.  codes 16-byte aligned. */
+int moe_mx8_quantize(const void* x, int T, int H, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
 /* Which kernel family moe_grouped_ffn runs for a shape (the results are the same
  * computation either way): MOE_FFN_WEIGHT_STREAM (decode-sized batches: each
  * expert's weights stream once past its few tokens) or MOE_FFN_GROUPED_GEMM
  * (32 or more (token, expert) pairs per expert on average, bf16 or MXFP4 weights
- * with H, I and I_shared multiples of 128).  -1 for an invalid shape. */
+ * with H, I and I_shared multiples of 128; MOE_MXFP4_A8 always).  -1 for an
+ * invalid shape. */
 enum { MOE_FFN_WEIGHT_STREAM = 0, MOE_FFN_GROUPED_GEMM = 1 };
 int moe_grouped_ffn_kind(int T, int k, int E, int H, int I, int I_shared, int wdt);
 /* The two phases of moe_grouped_ffn, same arguments: gate_up writes the SwiGLU

@@ -47,7 +47,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
   } while (0)
 
 int check_dims(int wdt, int H, int I, const char* what) {
-  if (wdt < MOE_F32 || wdt > MOE_MXFP4) return fail(MOE_EINVAL, "%s: unknown weight type %d", what, wdt);
+  if (wdt < MOE_F32 || wdt > MOE_MXFP4_A8) return fail(MOE_EINVAL, "%s: unknown weight type %d", what, wdt);
   if (H <= 0 || I <= 0) return fail(MOE_EINVAL, "%s: H=%d and I=%d must be positive", what, H, I);
   const int q = wdt == MOE_F32 ? 4 : 32;
   if (H % q || I % q) return fail(MOE_EINVAL, "%s: H=%d and I=%d must be multiples of %d", what, H, I, q);
@@ -88,7 +88,8 @@ size_t moe_expert_bytes(int wdt, int H, int I) {
   switch (wdt) {
     case MOE_F32: return (size_t)4 * 3 * H * I;
     case MOE_BF16: return (H % 32 || I % 32) ? 0 : (size_t)2 * 3 * H * I;
-    case MOE_MXFP4: {
+    case MOE_MXFP4:
+    case MOE_MXFP4_A8: {
       if (H % 32 || I % 32) return 0;
       // tiled: 1 KB of codes per 16-row x 128-column tile (K padded to 128), and per
       // row tile one 1 KB scale block per 16 column steps
@@ -181,9 +182,8 @@ int moe_combine(const float* out_rows, const float* topk_w, const int32_t* inv_r
 // ---------------------------------------------------------------------------
 size_t moe_grouped_ffn_workspace(int T, int k, int E, int H, int I, int I_shared, int wdt) {
   (void)E;
-  (void)H;
-  if (T < 0 || k < 1 || I <= 0 || I_shared < 0 || wdt < MOE_F32 || wdt > MOE_MXFP4) return 0;
-  return moe::ffn_workspace_bytes(wdt, T, k, I, I_shared);
+  if (T < 0 || k < 1 || H <= 0 || I <= 0 || I_shared < 0 || wdt < MOE_F32 || wdt > MOE_MXFP4_A8) return 0;
+  return moe::ffn_workspace_bytes(wdt, T, k, H, I, I_shared);
 }
 
 namespace {
@@ -195,6 +195,7 @@ enum { PHASE_GATE_UP = 1, PHASE_DOWN = 2 };
 // thing.
 constexpr int64_t kPrefillMinPairs = 32;
 bool uses_prefill(int wdt, int T, int k, int E, int H, int I, int I_shared) {
+  if (wdt == MOE_MXFP4_A8) return true;  // the native FP4 path has only the grouped GEMM
   return (int64_t)T * k >= kPrefillMinPairs * E && moe::prefill_supported(wdt, H, I, I_shared);
 }
 
@@ -227,7 +228,9 @@ int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, 
   if (!expert_addr)
     REQUIRE(slot_stride >= eb && slot_stride % 16 == 0,
             "slot_stride=%zu must be >= expert bytes %zu and a multiple of 16", slot_stride, eb);
-  const size_t need = moe::ffn_workspace_bytes(wdt, T, k, I, I_shared);
+  if (wdt == MOE_MXFP4_A8 && !moe::prefill_supported(MOE_MXFP4, H, I, I_shared))
+    return fail(MOE_EUNSUPPORTED, "MXFP4 weights with MXFP8 activations need H, I and I_shared multiples of 128");
+  const size_t need = moe::ffn_workspace_bytes(wdt, T, k, H, I, I_shared);
   if (ws_bytes < need) return fail(MOE_ECAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, need);
   moe::FfnArgs a;
   a.slot_pool = static_cast<const uint8_t*>(slot_pool);
@@ -250,7 +253,26 @@ int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, 
   a.h_ld = I > I_shared ? I : I_shared;
   a.routed_items = (int)((int64_t)T * k < E ? (int64_t)T * k : E);
   a.lds_rows = 0;  // set per launch by the decode launchers
+  a.xq = nullptr;
+  a.xs = nullptr;
   const bool prefill = uses_prefill(wdt, T, k, E, H, I, I_shared);
+  if (wdt == MOE_MXFP4_A8) {
+    // native FP4 path: x -> MXFP8 in the workspace, gate_up on the scaled MFMA, down
+    // as the MXFP4 grouped GEMM (bf16 intermediate)
+    uint8_t* xq = static_cast<uint8_t*>(workspace) + moe::ffn_workspace_xq_offset(T, k, I, I_shared);
+    a.xq = xq;
+    a.xs = xq + (size_t)T * H;
+    if (phases & PHASE_GATE_UP) {
+      hipError_t e = moe::launch_mx8_quantize(static_cast<const uint16_t*>(x), T, H, xq, xq + (size_t)T * H, stream);
+      if (e == hipSuccess) e = moe::launch_native_gate_up(a, stream);
+      if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn native gate_up launch");
+    }
+    if (phases & PHASE_DOWN) {
+      hipError_t e = moe::launch_prefill_down(MOE_MXFP4, a, stream);
+      if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn down launch");
+    }
+    return MOE_OK;
+  }
   if (phases & PHASE_GATE_UP) {
     hipError_t e = prefill ? moe::launch_prefill_gate_up(wdt, a, stream) : moe::launch_ffn_gate_up(wdt, a, stream);
     if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn gate_up launch");
@@ -271,9 +293,20 @@ int moe_grouped_ffn_addr(int wdt, const uint64_t* expert_addr, const void* share
                      T, k, E, H, I, out_rows, shared_out, workspace, ws_bytes, stream, expert_addr);
 }
 
+int moe_mx8_quantize(const void* x, int T, int H, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  if (T < 0 || H <= 0 || H % 32) return fail(MOE_EINVAL, "moe_mx8_quantize: T=%d, H=%d (a multiple of 32)", T, H);
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(codes);
+  if (!scales) return fail(MOE_EINVAL, "scales must not be null");
+  hipError_t e = moe::launch_mx8_quantize(static_cast<const uint16_t*>(x), T, H, codes, scales, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_mx8_quantize launch");
+}
+
 int moe_grouped_ffn_kind(int T, int k, int E, int H, int I, int I_shared, int wdt) {
   if (check_routing(T, E, k) || check_dims(wdt, H, I, "moe_grouped_ffn_kind")) return -1;
   if (I_shared && check_dims(wdt, H, I_shared, "moe_grouped_ffn_kind shared expert")) return -1;
+  if (wdt == MOE_MXFP4_A8 && !moe::prefill_supported(MOE_MXFP4, H, I, I_shared)) return -1;
   return uses_prefill(wdt, T, k, E, H, I, I_shared) ? MOE_FFN_GROUPED_GEMM : MOE_FFN_WEIGHT_STREAM;
 }
 
@@ -348,7 +381,7 @@ int moe_grouped_ffn_noalloc(int wdt, const void* slot_pool, size_t slot_stride, 
   if (int rc = check_routing(T, E, k)) return rc;
   if (int rc = check_dims(wdt, H, I, "moe_grouped_ffn_noalloc")) return rc;
   if (I_shared < 0) return fail(MOE_EINVAL, "moe_grouped_ffn_noalloc: I_shared=%d < 0", I_shared);
-  const size_t need = moe::ffn_workspace_bytes(wdt, T, k, I, shared_w ? I_shared : 0);
+  const size_t need = moe::ffn_workspace_bytes(wdt, T, k, H, I, shared_w ? I_shared : 0);
   if (need > MOE_NOALLOC_SCRATCH_BYTES)
     return fail(MOE_ECAPACITY, "moe_grouped_ffn_noalloc: the intermediate needs %zu bytes, more than the %zu of "
                 "the fixed scratch array", need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);

@@ -24,6 +24,8 @@ struct FfnArgs {
   const uint64_t* expert_addr;    // [E] address of each expert's weights (0: not computed), or null
   const uint8_t* shared_w;        // nullable
   const void* x;                  // [T][H] f32 or bf16
+  const uint8_t* xq;              // MXFP8 activations: [T][H] E4M3 codes of x (native FP4 path)
+  const uint8_t* xs;              //                    [T][H/32] E8M0 block scales
   const int32_t* offsets;         // [E+1]
   const int32_t* sorted_rows;     // [T*k]
   float* out_rows;                // [T*k][H]
@@ -86,7 +88,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+// SiLU z * sigmoid(z) = z / (1 + e^-z), from the hardware's base-2 exponential
+// (e^-z = 2^(-z log2 e)) and reciprocal, each within about one f32 ulp: far below
+// the bf16 rounding of the gate/up product that follows, and a few instructions
+// instead of a range-reduced exponential and an IEEE division.  Large negative z
+// gives 2^+inf = inf and z * 0 = -0, the limit.
+__device__ __forceinline__ float silu_f32(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {

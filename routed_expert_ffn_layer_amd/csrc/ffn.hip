@@ -44,18 +44,13 @@ static void launch_ffn_kernel(K kernel, unsigned grid, hipStream_t st, Args... a
 }
 // Waves per block of the MFMA decode kernels: bf16 splits K over up to 4 waves of a
 // block; MXFP4 (no K split) uses 4 with one token tile (the block stages the
-// tokens once for 4 waves) and MOE_DEC_MXN_WPB with more (smaller blocks even out
-// the work per CU: one-wave blocks measured 14% faster at 64 tokens).
-#ifndef MOE_DEC_MX1_WPB
-#define MOE_DEC_MX1_WPB 4
-#endif
-#ifndef MOE_DEC_MXN_WPB
-#define MOE_DEC_MXN_WPB 1
-#endif
+// tokens once for 4 waves) and 1 with more (smaller blocks even out the work per
+// CU: one-wave blocks measured 14% faster at 64 tokens).
+constexpr int kDecMx1Wpb = 4, kDecMxNWpb = 1;
 template <int WT, int NT>
-constexpr int dec_wpb() { return WT == W_MXFP4 ? (NT == 1 ? MOE_DEC_MX1_WPB : MOE_DEC_MXN_WPB) : 4; }
+constexpr int dec_wpb() { return WT == W_MXFP4 ? (NT == 1 ? kDecMx1Wpb : kDecMxNWpb) : 4; }
 static int dec_wpb_of(int wtype, int nt) {
-  return wtype == W_MXFP4 ? (nt == 1 ? MOE_DEC_MX1_WPB : MOE_DEC_MXN_WPB) : 4;
+  return wtype == W_MXFP4 ? (nt == 1 ? kDecMx1Wpb : kDecMxNWpb) : 4;
 }
 
 template <int WT, int NT, typename K, typename... Args>
@@ -122,43 +117,23 @@ __global__ __launch_bounds__(256) void down_f32(FfnArgs a, int shared_tiles, int
 // bf16 / MXFP4 weights on bf16 MFMA.
 // ===========================================================================
 // Register budget of the decode kernels.  A weight-streaming kernel needs many
-// waves' loads in flight; MXFP4 kernels are compiled for at least
-// MOE_DEC_MX1_WAVES (one token tile) or MOE_DEC_MXN_WAVES (more) waves per SIMD,
-// with their chunks shortened by MOE_DEC_MX1_DIV / MOE_DEC_MXN_DIV to fit.
-#ifndef MOE_UNROLL_SCALE
-#define MOE_UNROLL_SCALE 1
-#endif
-#ifndef MOE_DEC_MX1_WAVES
-#define MOE_DEC_MX1_WAVES 2
-#endif
-#ifndef MOE_DEC_MX1_DIV
-#define MOE_DEC_MX1_DIV 2
-#endif
-#ifndef MOE_DEC_MXN_WAVES
-#define MOE_DEC_MXN_WAVES 2
-#endif
-#ifndef MOE_DEC_MXN_DIV
-#define MOE_DEC_MXN_DIV 2
-#endif
-#ifndef MOE_DEC_RING
-#define MOE_DEC_RING 4
-#endif
-#ifndef MOE_DEC_LB_WAVES
-#define MOE_DEC_LB_WAVES 3
-#endif
-constexpr int kDecRing = MOE_DEC_RING;  // weight steps in flight per wave (token rows in LDS)
+// waves' loads in flight; MXFP4 kernels are compiled for at least 2 waves per
+// SIMD (3 for the kernels that read their token rows from LDS), with their chunks
+// of k steps halved to fit.
+constexpr int kDecMxWaves = 2, kDecMxLdsWaves = 3, kDecMxDiv = 2;
+constexpr int kDecRing = 4;  // weight steps in flight per wave (token rows in LDS)
 template <int WT, int NT, bool LB = false>
 struct DecTune {
   static constexpr bool mx = WT == W_MXFP4, mx1 = mx && NT == 1;
-  static constexpr int waves = mx && LB ? MOE_DEC_LB_WAVES : mx1 ? MOE_DEC_MX1_WAVES : mx ? MOE_DEC_MXN_WAVES : 1;
-  static constexpr int div = mx1 ? MOE_DEC_MX1_DIV : mx ? MOE_DEC_MXN_DIV : 1;
+  static constexpr int waves = mx && LB ? kDecMxLdsWaves : mx ? kDecMxWaves : 1;
+  static constexpr int div = mx ? kDecMxDiv : 1;
 };
 // k steps per chunk of loads (bounded by the registers two chunks take).
 template <int WT, int NT, int R>
 struct Unroll {
   static constexpr int raw = WT == W_MXFP4 ? (4 / (NT * R) > 0 ? 4 / (NT * R) : 1)
                                            : (8 / (NT * R) > 0 ? 8 / (NT * R) : 1);
-  static constexpr int scaled = MOE_UNROLL_SCALE * (raw > 4 ? 4 : raw) / DecTune<WT, NT>::div;
+  static constexpr int scaled = (raw > 4 ? 4 : raw) / DecTune<WT, NT>::div;
   static constexpr int value = scaled > 0 ? scaled : 1;
 };
 
@@ -658,9 +633,17 @@ __global__ __launch_bounds__((64 * dec_wpb<WT, NT>())) __attribute__((amdgpu_wav
 // ===========================================================================
 // Launchers
 // ===========================================================================
-size_t ffn_workspace_bytes(int wtype, int T, int k, int I, int I_shared) {
+size_t ffn_workspace_xq_offset(int T, int k, int I, int I_shared) {
   const size_t rows = (size_t)T * k + (I_shared > 0 ? (size_t)T : 0);
   const size_t ld = (size_t)(I > I_shared ? I : I_shared);
+  return (rows * ld * 2 + 255) / 256 * 256;
+}
+
+size_t ffn_workspace_bytes(int wtype, int T, int k, int H, int I, int I_shared) {
+  const size_t rows = (size_t)T * k + (I_shared > 0 ? (size_t)T : 0);
+  const size_t ld = (size_t)(I > I_shared ? I : I_shared);
+  if (wtype == 3)  // intermediate, then E4M3 codes [T][H] and E8M0 scales [T][H/32]
+    return ffn_workspace_xq_offset(T, k, I, I_shared) + (size_t)T * H + ((size_t)T * H / 32 + 255) / 256 * 256;
   return rows * ld * (wtype == W_F32 ? 4 : 2);
 }
 
@@ -673,48 +656,31 @@ size_t ffn_workspace_bytes(int wtype, int T, int k, int I, int I_shared) {
 struct Shape {
   int kw, r;
 };
-#ifndef MOE_DEC_MX1_R
-#define MOE_DEC_MX1_R 2
-#endif
-#ifndef MOE_DEC_MXN_R
-#define MOE_DEC_MXN_R 4
-#endif
+constexpr int kDecMx1R = 2, kDecMxNR = 4;  // MXFP4 row tiles per wave, T <= 16 / more
 static Shape gate_up_shape(int wtype, int T) {
   if (wtype == W_BF16) return T <= 4 ? Shape{4, 1} : Shape{2, 1};
-  return T <= 16 ? Shape{1, MOE_DEC_MX1_R} : Shape{1, MOE_DEC_MXN_R};
+  return T <= 16 ? Shape{1, kDecMx1R} : Shape{1, kDecMxNR};
 }
-#ifndef MOE_DEC_BF16_DN_KW
-#define MOE_DEC_BF16_DN_KW 1
-#endif
-#ifndef MOE_DEC_BF16_DN_R
-#define MOE_DEC_BF16_DN_R 2
-#endif
+constexpr int kDecBf16DnKw = 1, kDecBf16DnR = 2;  // bf16 down: waves splitting K, row tiles
 static Shape down_shape(int wtype, int T) {
-  if (wtype == W_BF16) return Shape{MOE_DEC_BF16_DN_KW, MOE_DEC_BF16_DN_R};
-  return T <= 16 ? Shape{1, MOE_DEC_MX1_R} : Shape{1, MOE_DEC_MXN_R};
+  if (wtype == W_BF16) return Shape{kDecBf16DnKw, kDecBf16DnR};
+  return T <= 16 ? Shape{1, kDecMx1R} : Shape{1, kDecMxNR};
 }
 
-#ifndef MOE_DEC_MX_NTMAX
-#define MOE_DEC_MX_NTMAX 2
-#endif
+constexpr int kDecMxNtMax = 2;  // MXFP4: token tiles per pass
 static int pick_nt(int T, int wtype) {
   const int nt = T <= 16 ? 1 : T <= 32 ? 2 : T <= 64 ? 4 : 8;
-  return wtype == W_MXFP4 && nt > MOE_DEC_MX_NTMAX ? MOE_DEC_MX_NTMAX : nt;
+  return wtype == W_MXFP4 && nt > kDecMxNtMax ? kDecMxNtMax : nt;
 }
 
 // MXFP4 passes of one token tile take their token rows from LDS (staged once per
 // pass and block): the launch's dynamic LDS holds as many rows of K columns as fit
-// in MOE_DEC_LDS_ROWS_MAX bytes (more would cap the blocks per CU), at most
+// in kDecLdsRowsMax bytes (more would cap the blocks per CU), at most
 // min(T, 16); a block whose pass has more rows reads them from memory instead.
-#ifndef MOE_DEC_LDS_ROWS_MAX
-#define MOE_DEC_LDS_ROWS_MAX 49152
-#endif
-#ifndef MOE_DEC_LDS_MIN_T
-#define MOE_DEC_LDS_MIN_T 1
-#endif
+constexpr size_t kDecLdsRowsMax = 49152;
 static int lds_rows_for(int T, int K) {
-  if (T < MOE_DEC_LDS_MIN_T) return 0;
-  const int fit = (int)(MOE_DEC_LDS_ROWS_MAX / ((size_t)K * 2 + 16));
+  if (T < 1) return 0;
+  const int fit = (int)(kDecLdsRowsMax / ((size_t)K * 2 + 16));
   const int want = T < 16 ? T : 16;
   return fit < want ? fit : want;
 }
@@ -796,7 +762,7 @@ hipError_t launch_ffn_down(int wtype, const FfnArgs& a, hipStream_t st) {
   const int shared_tiles = sh ? tiles : 0;
   const unsigned grid = shared_tiles + a.routed_items * tiles;
   if (!grid) return hipSuccess;
-  if (wtype == W_BF16) dn_nt<W_BF16, MOE_DEC_BF16_DN_KW, MOE_DEC_BF16_DN_R>(a, st, grid, shared_tiles, tiles);
+  if (wtype == W_BF16) dn_nt<W_BF16, kDecBf16DnKw, kDecBf16DnR>(a, st, grid, shared_tiles, tiles);
   else if (sp.r == 1) dn_nt<W_MXFP4, 1, 1>(a, st, grid, shared_tiles, tiles);
   else if (sp.r == 2) dn_nt<W_MXFP4, 1, 2>(a, st, grid, shared_tiles, tiles);
   else dn_nt<W_MXFP4, 1, 4>(a, st, grid, shared_tiles, tiles);

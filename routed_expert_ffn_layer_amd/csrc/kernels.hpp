@@ -28,14 +28,22 @@ constexpr int kMoveBatch = 480;
 hipError_t launch_move_slots(const uint8_t* src, uint64_t src_stride, uint8_t* dst, uint64_t dst_stride,
                              uint64_t bytes, const int32_t* from, const int32_t* to, int n, hipStream_t st);
 
-// Grouped FFN phases.  wtype: 0 f32, 1 bf16, 2 mxfp4.
+// Grouped FFN phases.  wtype: 0 f32, 1 bf16, 2 mxfp4 (3, MXFP4 with MXFP8
+// activations, runs the grouped GEMM only).
 hipError_t launch_ffn_gate_up(int wtype, const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_down(int wtype, const FfnArgs& a, hipStream_t st);
 // Prefill-sized batches (LDS-staged token tiles); same arguments and results.
 bool prefill_supported(int wtype, int H, int I, int I_shared);
 hipError_t launch_prefill_gate_up(int wtype, const FfnArgs& a, hipStream_t st);
 hipError_t launch_prefill_down(int wtype, const FfnArgs& a, hipStream_t st);
-// Workspace bytes (the SwiGLU intermediate for T*k routed + T shared rows).
-size_t ffn_workspace_bytes(int wtype, int T, int k, int I, int I_shared);
+// Native FP4 path: MXFP8 activations (E4M3 codes [T][H], E8M0 scales [T][H/32])
+// from bf16 x, then gate_up on the scaled f8f6f4 MFMA (a.xq, a.xs); the down phase
+// is launch_prefill_down with MXFP4 weights.
+hipError_t launch_mx8_quantize(const uint16_t* x, int T, int H, uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_native_gate_up(const FfnArgs& a, hipStream_t st);
+// Workspace bytes: the SwiGLU intermediate for T*k routed + T shared rows; for the
+// native path (wtype 3) also the MXFP8 activations, at ffn_workspace_xq_offset.
+size_t ffn_workspace_bytes(int wtype, int T, int k, int H, int I, int I_shared);
+size_t ffn_workspace_xq_offset(int T, int k, int I, int I_shared);
 
 }  // namespace moe

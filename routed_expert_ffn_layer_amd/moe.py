@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "lib", "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EHIP, MOE_ENOMEM, MOE_ESTATE = range(7)
-MOE_F32, MOE_BF16, MOE_MXFP4 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_MXFP4, MOE_MXFP4_A8 = 0, 1, 2, 3
 
 _lib = None
 
@@ -55,7 +55,7 @@ EXPORTS = ["moe_abi_version", "moe_status_str", "moe_last_error", "moe_expert_by
            "moe_cache_lookup_host", "moe_cache_state", "moe_cache_inject_fill_failure",
            "moe_cache_lookup_fill_split", "moe_cache_wait_fills", "moe_cache_set_fill_fraction",
            "moe_cache_lookup_fill_inplace", "moe_cache_step_inplace", "moe_grouped_ffn_addr", "moe_route", "moe_cache_resize", "moe_route_project",
-           "moe_grouped_ffn_workspace", "moe_grouped_ffn_kind", "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down", "moe_grouped_ffn_noalloc",
+           "moe_grouped_ffn_workspace", "moe_grouped_ffn_kind", "moe_mx8_quantize", "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down", "moe_grouped_ffn_noalloc",
            "moe_combine", "moe_layer_stream_create", "moe_layer_stream_destroy", "moe_layer_stream_fill",
            "moe_layer_stream_acquire", "moe_layer_stream_release"]
 
@@ -94,6 +94,7 @@ def lib():
     L.moe_cache_inject_fill_failure.argtypes = [P, ctypes.c_int64]
     L.moe_grouped_ffn_workspace.restype = sz
     L.moe_grouped_ffn_kind.argtypes = [i, i, i, i, i, i, i]
+    L.moe_mx8_quantize.argtypes = [P, i, i, P, P, P]
     L.moe_grouped_ffn_workspace.argtypes = [i, i, i, i, i, i, i]
     ffn_args = [i, P, sz, P, P, i, P, P, P, i, i, i, i, i, P, P, P, sz, P]
     L.moe_grouped_ffn.argtypes = ffn_args
@@ -166,6 +167,11 @@ def moe_grouped_ffn_workspace(T, k, E, H, I, I_shared, wdt):
 
 
 MOE_FFN_WEIGHT_STREAM, MOE_FFN_GROUPED_GEMM = 0, 1
+
+
+def moe_mx8_quantize(x, codes, scales, stream=None):
+    T, H = x.shape
+    _check(lib().moe_mx8_quantize(_ptr(x), T, H, _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def moe_grouped_ffn_kind(T, k, E, H, I, I_shared, wdt):
