@@ -50,7 +50,8 @@ METRIC = "MoE-layer tokens/s at 1 MI355X; % HBM BW (decode), % MFMA peak (prefil
 COUNTERS = {
     "decode_bf16": ("gate_up_mfma_bf16_decode_T16_counters.txt", "gate_up_mfma"),
     "decode_mxfp4": ("gate_up_mfma_mxfp4_decode_T64_counters.txt", "gate_up_mfma"),
-    "prefill_mxfp4": ("prefill_gate_up_mxfp4_T4096_counters.txt", "prefill_gate_up"),
+    "prefill_mxfp4": ("grouped_gate_up_mxfp4_T4096_counters.txt", "grouped_gate_up"),
+    "prefill_mxfp4_a8": ("grouped_gate_up_native_fp4_T8192_counters.txt", "grouped_gate_up"),
 }
 FFN_SOURCES = [os.path.join(ROOT, "routed_expert_ffn_layer_amd", "csrc", f)
                for f in ("ffn.hip", "ffn_prefill.hip", "ffn_common.hpp", "common.hpp")]
@@ -176,7 +177,9 @@ def summarize_pmc(prof_dir):
     MFMA busy fraction SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs * 256 CUs
     * 4 SIMDs) where both counters were collected in the same run (both arrive
     summed over the GPU's instances: GRBM_GUI_ACTIVE once per XCD, the MFMA busy
-    cycles once per SIMD)."""
+    cycles once per SIMD).  Where a run also traced kernels (--kernel-trace), the
+    median core clock of the kernel's dispatches (GRBM_GUI_ACTIVE per XCD over the
+    dispatch's duration) and that clock over the 2.4 GHz of the spec peaks."""
     import csv
     import glob
     import re
@@ -189,6 +192,13 @@ def summarize_pmc(prof_dir):
             disp = r.get("Dispatch_Id", r.get("Correlation_Id"))
             per.setdefault(key, {}).setdefault(disp, 0.0)
             per[key][disp] += float(r["Counter_Value"])
+    # kernel-trace durations of the same runs (when the pass also traced kernels)
+    dur = {}
+    for f in glob.glob(os.path.join(prof_dir, "**", "*kernel_trace.csv"), recursive=True):
+        run = os.path.relpath(os.path.dirname(f), prof_dir).split(os.sep)[0]
+        for r in csv.DictReader(open(f)):
+            dur[(run, r.get("Dispatch_Id", r.get("Correlation_Id")))] = (
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
     out = {}
     for (run, name, ctr), d in sorted(per.items()):
         out.setdefault(name, {}).setdefault(run, {})[ctr] = {"per_dispatch": sum(d.values()) / len(d),
@@ -198,6 +208,19 @@ def summarize_pmc(prof_dir):
             if "SQ_VALU_MFMA_BUSY_CYCLES" in ctrs and "GRBM_GUI_ACTIVE" in ctrs:
                 ctrs["mfma_busy_frac"] = (ctrs["SQ_VALU_MFMA_BUSY_CYCLES"]["per_dispatch"] /
                                           (ctrs["GRBM_GUI_ACTIVE"]["per_dispatch"] / 8 * 256 * 4))
+            grbm = per.get((run, name, "GRBM_GUI_ACTIVE"))
+            if grbm:
+                # core clock of each dispatch: its GUI-active cycles per XCD over its
+                # traced duration; the spec peaks assume 2.4 GHz
+                # (only dispatches of 300 us or more: the counter window adds cycles
+                # outside the traced kernel, which short dispatches overstate)
+                clk = sorted(v / 8 / dur[(run, disp)] / 1e9 for disp, v in grbm.items()
+                             if (run, disp) in dur and dur[(run, disp)] >= 300e-6)
+                ds = sorted(dur[(run, disp)] for disp in grbm if (run, disp) in dur)
+                if clk:
+                    ctrs["median_duration_us"] = ds[len(ds) // 2] * 1e6
+                    ctrs["clock_ghz_median"] = clk[len(clk) // 2]
+                    ctrs["clock_limited_peak_frac"] = clk[len(clk) // 2] / 2.4
     return out
 
 
@@ -842,7 +865,7 @@ def workload_prefill_mxfp4(args, native=False):
         {"kernel": ("mx8_quantize + grouped_gate_up<native fp4 x fp8>" if native else
                     "grouped_gate_up<mxfp4> (moe_grouped_ffn_gate_up)"), "bound": "mfma", "achieved": gu_tf,
          "peak": peak, "unit": "TFLOP/s", "frac": gu_tf / peak,
-         "traffic": None if native else measured_traffic("prefill_mxfp4"),
+         "traffic": measured_traffic("prefill_mxfp4_a8" if native else "prefill_mxfp4"),
          "avg_launch_us": gu * 1e6, "algorithmic_flop_per_launch": gu_flop, "launches_timed": 10,
          "timing": "events around back-to-back gate_up launches on one layer's routing"},
         cpu,
