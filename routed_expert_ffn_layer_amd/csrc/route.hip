@@ -26,10 +26,11 @@ __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
 }
 
 // Top-k of one token row (all 64 lanes of the wave take part); lane j < k writes
-// the j-th winner and its gate weight to ids_out[j], w_out[j].
+// the j-th winner and its gate weight to ids_out[j], w_out[j], and returns the
+// winner's id (lanes j >= k return 0).
 template <int EPL>
-__device__ __forceinline__ void topk_row(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids_out,
-                                         float* __restrict__ w_out) {
+__device__ __forceinline__ int topk_row(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids_out,
+                                        float* __restrict__ w_out) {
   const int lane = threadIdx.x & 63;
   float v[EPL];
 #pragma unroll
@@ -75,6 +76,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int E, i
     ids_out[lane] = my_id;
     w_out[lane] = ex / s;
   }
+  return my_id;
 }
 
 template <int EPL>
@@ -302,8 +304,74 @@ __global__ __launch_bounds__(kPermThreads) void route_kernel(const float* __rest
   permute_block(ids, T * k, E, counts, offsets, sorted_rows, inv_rows);
 }
 
+// Top-k and permutation of a decode batch (T <= 8 tokens, T*k <= 64 pairs) in one
+// small workgroup: wave t takes token t's top-k as above (the tokens in parallel),
+// the ids meet in LDS behind one barrier, and wave 0 permutes the pairs in
+// registers: lane p holds pair p = t*k + j, and one pass over the pairs (each
+// broadcast with readlane) gives every lane the count and the number of smaller
+// ids of its experts e = i*64 + lane (counts, offsets) and its own pair's place,
+// the pairs of smaller experts plus those of the same expert with a smaller index
+// (the stable order by r).  Ids lie in [0, E) here (they come from top-k).
+constexpr int kRouteSmallMaxT = 8;
+template <int EPL>
+__global__ __launch_bounds__(64 * kRouteSmallMaxT) void route_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows,
+    int32_t* __restrict__ inv_rows) {
+  __shared__ int s_ids[64];
+  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+  if (t < T) {
+    const int id = topk_row<EPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+    if (lane < k) s_ids[t * k + lane] = id;
+  }
+  __syncthreads();
+  if (t != 0) return;
+  const int n = T * k;
+  const int my_e = lane < n ? s_ids[lane] : 0;
+  int cnt[EPL], below[EPL], place = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) cnt[i] = below[i] = 0;
+  for (int q = 0; q < n; ++q) {
+    const int eq = __builtin_amdgcn_readlane(my_e, q);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = i * 64 + lane;
+      cnt[i] += eq == e;
+      below[i] += eq < e;
+    }
+    place += eq < my_e || (eq == my_e && q < lane);
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = i * 64 + lane;
+    if (e < E) {
+      counts[e] = cnt[i];
+      offsets[e] = below[i];
+    }
+  }
+  if (lane == 0) offsets[E] = n;
+  if (lane < n) {
+    sorted_rows[place] = lane;
+    inv_rows[lane] = place;
+  }
+}
+
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_rows, int32_t* inv_rows, hipStream_t st) {
+  if (T <= kRouteSmallMaxT && T * k <= 64) {
+    const dim3 grid(1), block(64 * (T > 0 ? T : 1));
+    if (E <= 64)
+      hipLaunchKernelGGL(route_small_kernel<1>, grid, block, 0, st, logits, T, E, k, ids, w, counts, offsets, sorted_rows, inv_rows);
+    else if (E <= 128)
+      hipLaunchKernelGGL(route_small_kernel<2>, grid, block, 0, st, logits, T, E, k, ids, w, counts, offsets, sorted_rows, inv_rows);
+    else if (E <= 256)
+      hipLaunchKernelGGL(route_small_kernel<4>, grid, block, 0, st, logits, T, E, k, ids, w, counts, offsets, sorted_rows, inv_rows);
+    else if (E <= 512)
+      hipLaunchKernelGGL(route_small_kernel<8>, grid, block, 0, st, logits, T, E, k, ids, w, counts, offsets, sorted_rows, inv_rows);
+    else
+      hipLaunchKernelGGL(route_small_kernel<16>, grid, block, 0, st, logits, T, E, k, ids, w, counts, offsets, sorted_rows, inv_rows);
+    return hipGetLastError();
+  }
   if (T > kRouteFusedMaxT) {
     hipError_t e = launch_topk(logits, T, E, k, ids, w, st);
     if (e != hipSuccess) return e;

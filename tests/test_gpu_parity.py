@@ -54,11 +54,17 @@ def test_topk_matches_oracle(ora, case):
 
 
 @pytest.mark.parametrize("T,k,E", [(0, 4, 16), (1, 8, 256), (8, 6, 256), (64, 16, 1024), (65, 6, 256), (17, 2, 8),
-                                   (300, 8, 256), (5, 1, 1), (40, 3, 100)])
+                                   (300, 8, 256), (5, 1, 1), (40, 3, 100),
+                                   # small-batch kernel (T <= 8, T*k <= 64): exactly 64 pairs, E = 1024,
+                                   # ragged E, k = 32; the larger fused kernel: 8 tokens of 16 pairs
+                                   (8, 8, 256), (2, 16, 1024), (3, 4, 300), (1, 32, 64), (7, 9, 40), (64, 1, 64),
+                                   (8, 16, 256)])
 def test_route_fused_matches_separate_calls_and_oracle(ora, T, k, E):
-    """moe_route (one workgroup launch up to 64 tokens) = moe_route_topk + moe_permute
-    bit for bit, and the oracle's routing and permutation; logits rounded to a
-    coarse grid so that ties occur."""
+    """moe_route (one launch up to 8 tokens: a register permutation up to 64
+    (token, expert) pairs, else the workgroup one; separate launches above) =
+    moe_route_topk + moe_permute bit for bit,
+    and the oracle's routing and permutation; logits rounded to a coarse grid so
+    that ties occur."""
     log(f"route T={T} k={k} E={E}")
     g = np.random.default_rng(900 + T + E)
     logits = (np.round(g.standard_normal((T, E)) * 4) / 4).astype(np.float32)
