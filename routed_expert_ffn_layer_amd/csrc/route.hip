@@ -13,70 +13,106 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Top-k: one wave64 per token.  Lane l holds the logits of experts i*64 + l.
-// k rounds of a wave-wide argmax (butterfly over __shfl_xor) under the order
-// "larger logit first, equal logits to the lower index" (IEEE compare, so -0.0
-// equals +0.0); the winner's owner lane marks it taken.  Lane j keeps the j-th
-// winner; the gate weights are a max-subtracted softmax over those k values.
+// Top-k: one wave64 per token.  Lane l holds the logits of experts i*64 + l.  The
+// order is "larger logit first, equal logits to the lower index" (IEEE compare, so
+// -0.0 equals +0.0).  Logits become unsigned keys that order the same way; a radix
+// select finds the k-th largest key bit by bit from the top (32 rounds of a compare
+// and a ballot count, no cross-lane shuffles); the winners are every key above it
+// plus the keys equal to it in ascending expert index until there are k.  They are
+// compacted (ascending index) into a small per-wave LDS list, and each of the k
+// lanes finds its winner's output position by counting the winners ranked before
+// it.  The gate weights are a max-subtracted softmax over the k values.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-  if (ia == INT_MAX) return false;
-  if (ib == INT_MAX) return true;
-  return va > vb || (va == vb && ia < ib);
+// Orderable key of a finite logit: larger value -> larger key, -0.0 and +0.0 the
+// same key; 0 lies below every finite value and marks lanes past E.
+__device__ __forceinline__ uint32_t logit_key(float v) {
+  const uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Top-k of one token row (all 64 lanes of the wave take part); lane j < k writes
-// the j-th winner and its gate weight to ids_out[j], w_out[j], and returns the
-// winner's id (lanes j >= k return 0).
+constexpr int kTopkMaxWaves = 16;  // waves per block of the kernels that call topk_row
+constexpr int kTopkMaxK = 32;
+
+struct TopkLane {
+  int id;   // lane j < k: a winner's expert id
+  int pos;  // and its output position (rank among the winners)
+};
+
+// Top-k of one token row (all 64 lanes of the wave take part); writes the k winners
+// and their gate weights to ids_out[0..k), w_out[0..k) in order.  Lane j < k
+// returns one winner and its position (every position once).
 template <int EPL>
-__device__ __forceinline__ int topk_row(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids_out,
-                                        float* __restrict__ w_out) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ TopkLane topk_row(const float* __restrict__ row, int E, int k,
+                                             int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+  __shared__ uint32_t s_key[kTopkMaxWaves][kTopkMaxK];
+  __shared__ int s_id[kTopkMaxWaves][kTopkMaxK];
+  __shared__ float s_val[kTopkMaxWaves][kTopkMaxK];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   float v[EPL];
+  uint32_t key[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = i * 64 + lane;
     v[i] = e < E ? row[e] : 0.0f;
+    key[i] = e < E ? logit_key(v[i]) : 0u;
   }
-  uint32_t taken = 0;
-  float my_z = 0.0f;
+  // the k-th largest key: the largest t with at least k keys >= t
+  uint32_t thr = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = thr | (1u << b);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) c += __popcll(__ballot(key[i] >= cand));
+    if (c >= k) thr = cand;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) gt += __popcll(__ballot(key[i] > thr));
+  // winners in ascending expert index: keys above thr, and the first k - gt keys equal to it
+  int ties = 0, before = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const bool eq = key[i] == thr;
+    const uint64_t eqm = __ballot(eq);
+    const bool win = key[i] > thr || (eq && ties + __popcll(eqm & lanes_below) < k - gt);
+    const uint64_t wm = __ballot(win);
+    if (win) {
+      const int at = before + __popcll(wm & lanes_below);
+      s_key[wv][at] = key[i];
+      s_id[wv][at] = i * 64 + lane;
+      s_val[wv][at] = v[i];
+    }
+    ties += __popcll(eqm);
+    before += __popcll(wm);
+  }
+  __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in order
+  uint32_t my_key = 0;
   int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = 0.0f;
-    int be = INT_MAX;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = i * 64 + lane;
-      if (e < E && !((taken >> i) & 1u) && ranks_before(v[i], e, bv, be)) {
-        bv = v[i];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const float ov = __shfl_xor(bv, d, 64);
-      const int oe = __shfl_xor(be, d, 64);
-      if (ranks_before(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) {
-      my_z = bv;
-      my_id = be;
-    }
+  float my_v = 0.0f;
+  if (lane < k) {
+    my_key = s_key[wv][lane];
+    my_id = s_id[wv][lane];
+    my_v = s_val[wv][lane];
   }
-  const float z0 = __shfl(my_z, 0, 64);
-  const float ex = lane < k ? expf(my_z - z0) : 0.0f;
+  // position: winners with a larger key, or the same key and a lower index (the
+  // list is in ascending index)
+  int pos = 0;
+  for (int q = 0; q < k; ++q) {
+    const uint32_t kq = (uint32_t)__builtin_amdgcn_readlane((int)my_key, q);
+    pos += kq > my_key || (kq == my_key && q < lane);
+  }
+  const int top = __builtin_ctzll(__ballot(lane < k && pos == 0));
+  const float z0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), top));
+  const float ex = lane < k ? expf(my_v - z0) : 0.0f;
   float s = ex;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
   if (lane < k) {
-    ids_out[lane] = my_id;
-    w_out[lane] = ex / s;
+    ids_out[pos] = my_id;
+    w_out[pos] = ex / s;
   }
-  return my_id;
+  return TopkLane{my_id, pos};
 }
 
 template <int EPL>
@@ -321,8 +357,8 @@ __global__ __launch_bounds__(64 * kRouteSmallMaxT) void route_small_kernel(
   __shared__ int s_ids[64];
   const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
   if (t < T) {
-    const int id = topk_row<EPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
-    if (lane < k) s_ids[t * k + lane] = id;
+    const TopkLane r = topk_row<EPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+    if (lane < k) s_ids[t * k + r.pos] = r.id;
   }
   __syncthreads();
   if (t != 0) return;
