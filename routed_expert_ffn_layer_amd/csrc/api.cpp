@@ -2,6 +2,7 @@
 // error reporting, kernel dispatch, the device side of the expert-slot cache
 // (fills on a side stream fenced by events) and the prefill layer streamer.
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -14,6 +15,15 @@
 #include "cache_core.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
+
+// A roctx range around every call of the C ABI, named by the entry point, for
+// rocprofv3 --marker-trace (a no-op when no tool is attached).
+struct CallRange {
+  explicit CallRange(const char* name) { roctxRangePushA(name); }
+  ~CallRange() { roctxRangePop(); }
+  CallRange(const CallRange&) = delete;
+  CallRange& operator=(const CallRange&) = delete;
+};
 
 namespace {
 
@@ -69,6 +79,7 @@ extern "C" {
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
 const char* moe_status_str(int status) {
+  const CallRange range_(__func__);
   switch (status) {
     case MOE_OK: return "ok";
     case MOE_EINVAL: return "invalid argument";
@@ -84,6 +95,7 @@ const char* moe_status_str(int status) {
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 size_t moe_expert_bytes(int wdt, int H, int I) {
+  const CallRange range_(__func__);
   if (H <= 0 || I <= 0) return 0;
   switch (wdt) {
     case MOE_F32: return (size_t)4 * 3 * H * I;
@@ -103,6 +115,7 @@ size_t moe_expert_bytes(int wdt, int H, int I) {
 
 // ---------------------------------------------------------------------------
 int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  const CallRange range_(__func__);
   if (int rc = check_routing(T, E, k)) return rc;
   if (T == 0) return MOE_OK;
   REQUIRE_PTR(logits);
@@ -114,6 +127,7 @@ int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, 
 
 int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
                 int32_t* sorted_rows, int32_t* inv_rows, hipStream_t stream) {
+  const CallRange range_(__func__);
   if (int rc = check_routing(T, E, k)) return rc;
   REQUIRE_PTR(counts);
   REQUIRE_PTR(offsets);
@@ -128,6 +142,7 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, i
 
 int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w, int32_t* counts,
               int32_t* offsets, int32_t* sorted_rows, int32_t* inv_rows, hipStream_t stream) {
+  const CallRange range_(__func__);
   if (int rc = check_routing(T, E, k)) return rc;
   REQUIRE_PTR(counts);
   REQUIRE_PTR(offsets);
@@ -145,6 +160,7 @@ int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float
 int moe_route_project(const void* x, const void* w_router, int T, int H, int E, int k, float* logits,
                       int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_rows,
                       int32_t* inv_rows, hipStream_t stream) {
+  const CallRange range_(__func__);
   if (int rc = check_routing(T, E, k)) return rc;
   if (H <= 0 || H % 8) return fail(MOE_EINVAL, "moe_route_project: H=%d must be a positive multiple of 8", H);
   REQUIRE_PTR(counts);
@@ -167,6 +183,7 @@ int moe_route_project(const void* x, const void* w_router, int T, int H, int E, 
 
 int moe_combine(const float* out_rows, const float* topk_w, const int32_t* inv_rows, const float* shared_out, int T,
                 int k, int H, void* y, int ydt, hipStream_t stream) {
+  const CallRange range_(__func__);
   if (T < 0 || k < 1 || k > 32 || H <= 0 || H % 4) return fail(MOE_EINVAL, "moe_combine: bad T=%d k=%d H=%d", T, k, H);
   if (ydt != MOE_F32 && ydt != MOE_BF16) return fail(MOE_EINVAL, "moe_combine: ydt must be MOE_F32 or MOE_BF16");
   if (T == 0) return MOE_OK;
@@ -181,6 +198,7 @@ int moe_combine(const float* out_rows, const float* topk_w, const int32_t* inv_r
 
 // ---------------------------------------------------------------------------
 size_t moe_grouped_ffn_workspace(int T, int k, int E, int H, int I, int I_shared, int wdt) {
+  const CallRange range_(__func__);
   (void)E;
   if (T < 0 || k < 1 || H <= 0 || I <= 0 || I_shared < 0 || wdt < MOE_F32 || wdt > MOE_MXFP4_A8) return 0;
   return moe::ffn_workspace_bytes(wdt, T, k, H, I, I_shared);
@@ -289,11 +307,13 @@ int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, 
 int moe_grouped_ffn_addr(int wdt, const uint64_t* expert_addr, const void* shared_w, int I_shared, const void* x,
                          const int32_t* offsets, const int32_t* sorted_rows, int T, int k, int E, int H, int I,
                          float* out_rows, float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const CallRange range_(__func__);
   return grouped_ffn(PHASE_GATE_UP | PHASE_DOWN, wdt, nullptr, 0, nullptr, shared_w, I_shared, x, offsets, sorted_rows,
                      T, k, E, H, I, out_rows, shared_out, workspace, ws_bytes, stream, expert_addr);
 }
 
 int moe_mx8_quantize(const void* x, int T, int H, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const CallRange range_(__func__);
   if (T < 0 || H <= 0 || H % 32) return fail(MOE_EINVAL, "moe_mx8_quantize: T=%d, H=%d (a multiple of 32)", T, H);
   if (T == 0) return MOE_OK;
   REQUIRE_PTR(x);
@@ -304,6 +324,7 @@ int moe_mx8_quantize(const void* x, int T, int H, uint8_t* codes, uint8_t* scale
 }
 
 int moe_grouped_ffn_kind(int T, int k, int E, int H, int I, int I_shared, int wdt) {
+  const CallRange range_(__func__);
   if (check_routing(T, E, k) || check_dims(wdt, H, I, "moe_grouped_ffn_kind")) return -1;
   if (I_shared && check_dims(wdt, H, I_shared, "moe_grouped_ffn_kind shared expert")) return -1;
   if (wdt == MOE_MXFP4_A8 && !moe::prefill_supported(MOE_MXFP4, H, I, I_shared)) return -1;
@@ -314,6 +335,7 @@ int moe_grouped_ffn(int wdt, const void* slot_pool, size_t slot_stride, const in
                     const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
                     const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
                     float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const CallRange range_(__func__);
   return grouped_ffn(PHASE_GATE_UP | PHASE_DOWN, wdt, slot_pool, slot_stride, slot_of_expert, shared_w, I_shared, x,
                      offsets, sorted_rows, T, k, E, H, I, out_rows, shared_out, workspace, ws_bytes, stream);
 }
@@ -322,6 +344,7 @@ int moe_grouped_ffn_gate_up(int wdt, const void* slot_pool, size_t slot_stride, 
                             const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
                             const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
                             float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const CallRange range_(__func__);
   return grouped_ffn(PHASE_GATE_UP, wdt, slot_pool, slot_stride, slot_of_expert, shared_w, I_shared, x, offsets,
                      sorted_rows, T, k, E, H, I, out_rows, shared_out, workspace, ws_bytes, stream);
 }
@@ -330,6 +353,7 @@ int moe_grouped_ffn_down(int wdt, const void* slot_pool, size_t slot_stride, con
                          const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
                          const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
                          float* shared_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const CallRange range_(__func__);
   return grouped_ffn(PHASE_DOWN, wdt, slot_pool, slot_stride, slot_of_expert, shared_w, I_shared, x, offsets,
                      sorted_rows, T, k, E, H, I, out_rows, shared_out, workspace, ws_bytes, stream);
 }
@@ -378,6 +402,7 @@ int moe_grouped_ffn_noalloc(int wdt, const void* slot_pool, size_t slot_stride, 
                             const void* shared_w, int I_shared, const void* x, const int32_t* offsets,
                             const int32_t* sorted_rows, int T, int k, int E, int H, int I, float* out_rows,
                             float* shared_out, hipStream_t stream) {
+  const CallRange range_(__func__);
   if (int rc = check_routing(T, E, k)) return rc;
   if (int rc = check_dims(wdt, H, I, "moe_grouped_ffn_noalloc")) return rc;
   if (I_shared < 0) return fail(MOE_EINVAL, "moe_grouped_ffn_noalloc: I_shared=%d < 0", I_shared);
@@ -481,6 +506,7 @@ void invalidate_upto(moe_cache* c, size_t n_touched) {
 extern "C" {
 
 int moe_cache_create(const moe_cache_desc* d, moe_cache** out) {
+  const CallRange range_(__func__);
   if (!d || !out) return fail(MOE_EINVAL, "moe_cache_create: null argument");
   *out = nullptr;
   if (d->n_layers < 1 || d->n_experts < 1 || d->n_experts > 1024 || d->n_slots < 1)
@@ -519,6 +545,7 @@ int moe_cache_create(const moe_cache_desc* d, moe_cache** out) {
 }
 
 int moe_cache_destroy(moe_cache* c) {
+  const CallRange range_(__func__);
   if (!c) return MOE_OK;
   int rc = MOE_OK;
   if (c->device) {
@@ -547,12 +574,14 @@ int moe_cache_destroy(moe_cache* c) {
 }
 
 int moe_cache_inject_fill_failure(moe_cache* c, int64_t n) {
+  const CallRange range_(__func__);
   if (!c) return fail(MOE_EINVAL, "null cache");
   c->fail_after = n < 0 ? -1 : n;
   return MOE_OK;
 }
 
 int moe_cache_state(const moe_cache* c, int64_t* key_of_slot_host, int64_t* tick_of_slot_host) {
+  const CallRange range_(__func__);
   if (!c || !key_of_slot_host || !tick_of_slot_host) return fail(MOE_EINVAL, "moe_cache_state: null argument");
   c->core.state(key_of_slot_host, tick_of_slot_host);
   return MOE_OK;
@@ -560,6 +589,7 @@ int moe_cache_state(const moe_cache* c, int64_t* key_of_slot_host, int64_t* tick
 
 int moe_cache_lookup_host(moe_cache* c, int layer, const int32_t* counts_host, int wave, int32_t* slot_of_expert_host,
                           moe_fill* fills_host, int max_fills, int* n_fills_host, moe_cache_stats* stats_host) {
+  const CallRange range_(__func__);
   if (!c || !slot_of_expert_host || !n_fills_host) return fail(MOE_EINVAL, "moe_cache_lookup_host: null argument");
   if (wave == 0 && !counts_host) return fail(MOE_EINVAL, "moe_cache_lookup_host: counts_host is required for wave 0");
   int nacc = 0;
@@ -730,12 +760,14 @@ extern "C" {
 
 int moe_cache_lookup_fill(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_of_expert,
                           moe_cache_stats* stats_host, hipStream_t compute_stream) {
+  const CallRange range_(__func__);
   return lookup_fill_device(c, layer, counts, wave, slot_of_expert, nullptr, nullptr, stats_host, compute_stream,
                             "moe_cache_lookup_fill");
 }
 
 int moe_cache_lookup_fill_split(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_hits,
                                 int32_t* slot_misses, moe_cache_stats* stats_host, hipStream_t compute_stream) {
+  const CallRange range_(__func__);
   if (!slot_misses) return fail(MOE_EINVAL, "moe_cache_lookup_fill_split: null slot_misses");
   return lookup_fill_device(c, layer, counts, wave, slot_hits, slot_misses, nullptr, stats_host, compute_stream,
                             "moe_cache_lookup_fill_split");
@@ -744,12 +776,14 @@ int moe_cache_lookup_fill_split(moe_cache* c, int layer, const int32_t* counts, 
 int moe_cache_lookup_fill_inplace(moe_cache* c, int layer, const int32_t* counts, int wave, int32_t* slot_hits,
                                   int32_t* slot_misses, uint64_t* addr_inplace, moe_cache_stats* stats_host,
                                   hipStream_t compute_stream) {
+  const CallRange range_(__func__);
   if (!slot_misses || !addr_inplace) return fail(MOE_EINVAL, "moe_cache_lookup_fill_inplace: null table");
   return lookup_fill_device(c, layer, counts, wave, slot_hits, slot_misses, addr_inplace, stats_host,
                             compute_stream, "moe_cache_lookup_fill_inplace");
 }
 
 int moe_cache_set_fill_fraction(moe_cache* c, int num, int den) {
+  const CallRange range_(__func__);
   if (!c) return fail(MOE_EINVAL, "null cache");
   if (den < 1 || num < 0 || num > den)
     return fail(MOE_EINVAL, "moe_cache_set_fill_fraction: need 0 <= num <= den and den >= 1 (got %d/%d)", num, den);
@@ -759,6 +793,7 @@ int moe_cache_set_fill_fraction(moe_cache* c, int num, int den) {
 }
 
 int moe_cache_step_inplace(const moe_cache* c, int32_t* experts_host, int* n_host) {
+  const CallRange range_(__func__);
   if (!c || !experts_host || !n_host) return fail(MOE_EINVAL, "moe_cache_step_inplace: null argument");
   const std::vector<int32_t>& v = c->core.inplace();
   for (size_t i = 0; i < v.size(); ++i) experts_host[i] = v[i];
@@ -768,6 +803,7 @@ int moe_cache_step_inplace(const moe_cache* c, int32_t* experts_host, int* n_hos
 
 int moe_cache_resize(moe_cache* c, int n_slots, void* slot_pool, size_t slot_stride, int32_t* moved_from_host,
                      hipStream_t stream) {
+  const CallRange range_(__func__);
   if (!c) return fail(MOE_EINVAL, "null cache");
   if (n_slots < 1) return fail(MOE_EINVAL, "moe_cache_resize: n_slots=%d must be >= 1", n_slots);
   if (c->core.step_open()) return fail(MOE_ESTATE, "moe_cache_resize: a step is still open (finish its waves first)");
@@ -821,6 +857,7 @@ int moe_cache_resize(moe_cache* c, int n_slots, void* slot_pool, size_t slot_str
 }
 
 int moe_cache_wait_fills(moe_cache* c, hipStream_t compute_stream) {
+  const CallRange range_(__func__);
   if (!c) return fail(MOE_EINVAL, "null cache");
   if (!c->device) return fail(MOE_EINVAL, "moe_cache_wait_fills needs a device cache (slot_pool set)");
   if (!c->fill_pending) return MOE_OK;
@@ -846,6 +883,7 @@ struct moe_layer_stream {
 extern "C" {
 
 int moe_layer_stream_create(const moe_layer_stream_desc* d, moe_layer_stream** out) {
+  const CallRange range_(__func__);
   if (!d || !out) return fail(MOE_EINVAL, "moe_layer_stream_create: null argument");
   *out = nullptr;
   if (d->n_layers < 1 || d->layer_bytes == 0) return fail(MOE_EINVAL, "moe_layer_stream_create: bad sizes");
@@ -870,6 +908,7 @@ int moe_layer_stream_create(const moe_layer_stream_desc* d, moe_layer_stream** o
 }
 
 int moe_layer_stream_destroy(moe_layer_stream* s) {
+  const CallRange range_(__func__);
   if (!s) return MOE_OK;
   int rc = MOE_OK;
   for (int b = 0; b < 2; ++b) {
@@ -887,6 +926,7 @@ int moe_layer_stream_destroy(moe_layer_stream* s) {
 }
 
 int moe_layer_stream_fill(moe_layer_stream* s, int layer, int bank) {
+  const CallRange range_(__func__);
   if (!s) return fail(MOE_EINVAL, "null layer stream");
   if (layer < 0 || layer >= s->desc.n_layers || bank < 0 || bank > 1)
     return fail(MOE_EINVAL, "moe_layer_stream_fill: layer %d / bank %d out of range", layer, bank);
@@ -904,6 +944,7 @@ int moe_layer_stream_fill(moe_layer_stream* s, int layer, int bank) {
 }
 
 int moe_layer_stream_acquire(moe_layer_stream* s, int bank, hipStream_t compute_stream) {
+  const CallRange range_(__func__);
   if (!s || bank < 0 || bank > 1) return fail(MOE_EINVAL, "moe_layer_stream_acquire: bad argument");
   if (!s->filled[bank]) return fail(MOE_ESTATE, "moe_layer_stream_acquire: bank %d was never filled", bank);
   hipError_t e = hipStreamWaitEvent(compute_stream, s->ready[bank], 0);
@@ -911,6 +952,7 @@ int moe_layer_stream_acquire(moe_layer_stream* s, int bank, hipStream_t compute_
 }
 
 int moe_layer_stream_release(moe_layer_stream* s, int bank, hipStream_t compute_stream) {
+  const CallRange range_(__func__);
   if (!s || bank < 0 || bank > 1) return fail(MOE_EINVAL, "moe_layer_stream_release: bad argument");
   hipError_t e = hipEventRecord(s->released[bank], compute_stream);
   if (e != hipSuccess) return hip_fail(e, "moe_layer_stream_release");
