@@ -14,7 +14,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
-enum WType { W_F32 = 0, W_BF16 = 1, W_MXFP4 = 2 };
+// W_MXFP4_A8: MXFP4 weights whose gate/up activations are MXFP8 (the native FP4 x
+// FP8 path); the weights and their layout are W_MXFP4's.
+enum WType { W_F32 = 0, W_BF16 = 1, W_MXFP4 = 2, W_MXFP4_A8 = 3 };
 
 // Everything the grouped FFN kernels need, passed by value.
 struct FfnArgs {

@@ -642,7 +642,7 @@ size_t ffn_workspace_xq_offset(int T, int k, int I, int I_shared) {
 size_t ffn_workspace_bytes(int wtype, int T, int k, int H, int I, int I_shared) {
   const size_t rows = (size_t)T * k + (I_shared > 0 ? (size_t)T : 0);
   const size_t ld = (size_t)(I > I_shared ? I : I_shared);
-  if (wtype == 3)  // intermediate, then E4M3 codes [T][H] and E8M0 scales [T][H/32]
+  if (wtype == W_MXFP4_A8)  // intermediate, then E4M3 codes [T][H] and E8M0 scales [T][H/32]
     return ffn_workspace_xq_offset(T, k, I, I_shared) + (size_t)T * H + ((size_t)T * H / 32 + 255) / 256 * 256;
   return rows * ld * (wtype == W_F32 ? 4 : 2);
 }
