@@ -725,7 +725,37 @@ int lookup_fill_device(moe_cache* c, int layer, const int32_t* counts, int wave,
     c->fill_pending = split;
   }
   c->core.commit_wave(wave);
-  // slot table(s) upload through a ring of pinned staging buffers
+  // slot table(s): the wave's (expert, slot) pairs as the arguments of one small
+  // kernel when they fit (and no in-place address table is asked for), else an
+  // upload through a ring of pinned staging buffers
+  if (!addr_inplace) {
+    moe::SlotPairs sp;
+    sp.table_a = slot_a;
+    sp.table_b = split ? slot_misses : nullptr;
+    sp.E = E;
+    sp.n = 0;
+    bool fits = true;
+    for (int x = 0; x < E && fits; ++x) {
+      if (c->table[x] < 0) continue;
+      if (sp.n == moe::kSlotPairsMax) {
+        fits = false;
+        break;
+      }
+      sp.key[sp.n] = x;
+      sp.slot[sp.n] = c->table[x];
+      ++sp.n;
+    }
+    if (fits) {
+      if (split)
+        for (const moe::PlannedFill& f : c->fills)
+          for (int i = 0; i < sp.n; ++i)
+            if (sp.key[i] == f.expert) sp.key[i] |= 1 << 16;  // a filled expert: the misses' table
+      e = moe::launch_write_slot_tables(sp, compute_stream);
+      if (e != hipSuccess) return hip_fail(e, (std::string(what) + ": slot tables").c_str());
+      fill_stats(c, nacc, bytes, stats_host);
+      return MOE_OK;
+    }
+  }
   c->stage_next = (q + 1) % kStages;
   if (c->stage_used[q]) {
     e = hipEventSynchronize(c->stage_ev[q]);

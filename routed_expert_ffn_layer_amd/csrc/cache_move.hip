@@ -69,4 +69,27 @@ hipError_t launch_move_slots(const uint8_t* src, uint64_t src_stride, uint8_t* d
   return hipSuccess;
 }
 
+// Slot tables of one cache wave, written by a kernel whose arguments carry the
+// wave's (expert, slot) pairs: no staging copy of the whole table from host memory
+// (a small host-to-device copy runs as a runtime copy kernel that reads the host
+// buffer over the link).  Every entry of the table(s) becomes -1, then each pair is
+// written into table a or b; one block, so a barrier orders the two.
+__global__ __launch_bounds__(256) void write_slot_tables_kernel(SlotPairs p) {
+  for (int e = threadIdx.x; e < p.E; e += 256) {
+    p.table_a[e] = -1;
+    if (p.table_b) p.table_b[e] = -1;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < p.n; i += 256) {
+    const int e = p.key[i] & 0xffff;
+    int32_t* t = (p.key[i] >> 16) ? p.table_b : p.table_a;
+    t[e] = p.slot[i];
+  }
+}
+
+hipError_t launch_write_slot_tables(const SlotPairs& p, hipStream_t st) {
+  hipLaunchKernelGGL(write_slot_tables_kernel, dim3(1), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
 }  // namespace moe

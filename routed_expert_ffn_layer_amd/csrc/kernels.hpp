@@ -25,6 +25,18 @@ hipError_t launch_combine(const float* rows, const float* w, const int32_t* inv,
 // one pool to slot to[i] of another (batched launches, the table in the kernel
 // arguments).  Expert bytes must be a multiple of 16 and the pools 16-byte aligned.
 constexpr int kMoveBatch = 480;
+// The slot tables of one cache wave from up to kSlotPairsMax (expert, slot) pairs
+// passed by value: table_a (and table_b if non-null) [E] set to -1, then
+// key = expert | (table << 16) (table 0: a, 1: b) gets slot.  E <= 65535.
+constexpr int kSlotPairsMax = 240;
+struct SlotPairs {
+  int32_t* table_a;
+  int32_t* table_b;
+  int E, n;
+  int32_t key[kSlotPairsMax];
+  int32_t slot[kSlotPairsMax];
+};
+hipError_t launch_write_slot_tables(const SlotPairs& p, hipStream_t st);
 hipError_t launch_move_slots(const uint8_t* src, uint64_t src_stride, uint8_t* dst, uint64_t dst_stride,
                              uint64_t bytes, const int32_t* from, const int32_t* to, int n, hipStream_t st);
 
