@@ -268,3 +268,40 @@ def test_miss_split_bitwise_equal_to_resident(ora, fill):
     assert n_inplace > 0
     assert (n_fills == 0) == (fill == (0, 1))
     cache.close()
+
+
+@pytest.mark.parametrize("split", [False, True], ids=["whole", "split"])
+def test_wide_wave_slot_tables(ora, split):
+    """Waves that touch more experts than the slot-table kernel takes as arguments
+    (240): 256 experts, 200 tokens of top-6 (about 253 experts active), 300 slots,
+    so the first step's single wave fills about 250 experts and the slot tables go
+    through the pinned staging ring; later steps (fewer active experts) through the
+    argument kernel.  Bitwise against the all-resident layer, LRU state against the
+    oracle after every step."""
+    H, I, E, k, T, S = 128, 64, 256, 6, 200, 300
+    seed = 4242
+    experts = np.stack([synth.random_expert(synth.BF16, H, I, synth.rng(seed, 3, 0, e)) for e in range(E)])
+    eb = experts.shape[1]
+    host = _pinned_pool(experts)
+    cache, slot_pool, stride = _device_cache(1, E, S, eb, host)
+    lru = ora.LRU(S, 1, E)
+    resident = to_dev(experts)
+    wide = 0
+    for step, n in enumerate((T, 3, T, 1)):
+        x = to_dev(synth.encode_activations(synth.BF16, synth.normal_x(seed, n, H, step)))
+        lg = to_dev(synth.normal_logits(seed, n, E, step))
+        b = L.LayerBuffers(n, E, k, H, I, synth.BF16)
+        bc = L.LayerBuffers(n, E, k, H, I, synth.BF16)
+        y_ref = _resident_y(b, lg, x, resident, eb, E)
+        fwd = L.forward_cached_split if split else L.forward_cached
+        y, waves = fwd(bc, cache, 0, lg, x, slot_pool, stride)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), step
+        active = int((bc.counts > 0).sum().item())
+        wide += active > 240
+        log(f"  step {step}: {n} tokens, {active} active experts, {waves[0]['misses']} misses")
+        r = lru.step(0, bc.counts.cpu().numpy())
+        assert waves[0]["misses"] == int((r["hit"] == 0).sum())
+        _same_state(cache, lru)
+    assert wide >= 1
+    cache.close()
