@@ -32,11 +32,16 @@
 //    read is served 8 or 16 lanes at a time;
 //  * the loads of chunk c+3 are issued before chunk c is computed; every load is
 //    unconditional (past the end they re-read the last chunk), so each wave issues
-//    exactly NL loads per chunk and "chunk c+1 has landed" is the wait vmcnt(2 NL),
-//    followed by a barrier that makes the LDS rows visible.
+//    at least NL loads per chunk and "chunk c+1 has landed" is the wait vmcnt(2 NL),
+//    followed by a barrier that makes the LDS rows visible;
+//  * MXFP4 scales: each wave copies its tiles' E8M0 bytes for 32 chunks at a time
+//    into LDS (one 1 KB load per 16-row tile) and reads one byte per tile and chunk
+//    from there, instead of re-loading from memory, every chunk, a word that serves
+//    8 chunks (a load as costly to the memory pipeline as the code load beside it).
 // Measured on the MI355X (same box, MXFP4 gate_up at the 4096-token shape): this
 // shape 988-996 us, one wave per SIMD with 4 tiles per wave 1067 us, the earlier
-// 16x16x32 design 1080-1091 us.
+// 16x16x32 design 1080-1091 us; later, on another box, the scales in LDS 938-941 us
+// against 959 us for the per-chunk scale loads (913 us with no scale loads at all).
 // Blocks are ordered so that the blocks of one expert run together on one XCD
 // (blockIdx b executes on XCD b % 8), keeping its token rows in that XCD's L2.
 #include "ffn_common.hpp"
@@ -61,7 +66,6 @@ struct GConf {
   static constexpr int WT = WT_, W = W_, R = R_, D = D_, MAXNT = MAXNT_;
   static constexpr bool NATIVE = NATIVE_;
   static constexpr int LPT = WT == W_MXFP4 ? 1 : 4;  // 16-byte code loads per row tile and chunk
-  static constexpr int SPT = WT == W_MXFP4 ? 1 : 0;  // scale words per row tile and chunk
   static constexpr int ROWB = NATIVE ? kGKC : 2 * kGKC;  // bytes of one token row of a chunk
   static constexpr int RPP = 1024 / ROWB;            // token rows per 1 KB piece
   static constexpr int PASS = 32 * MAXNT;            // tokens per pass
@@ -69,6 +73,11 @@ struct GConf {
   // (the blocks of the chunk pair holding the chunk)
   static constexpr int ROWS_BYTES = PASS * ROWB;
   static constexpr int BUF = ROWS_BYTES + (NATIVE ? PASS * 4 : 0);  // bytes of one LDS ring slot
+  // MXFP4: after the ring, each wave's E8M0 weight scales, two windows of 32
+  // chunks (16 steps of 128 columns: one 1 KB scale block per 16-row tile)
+  static constexpr int WIN = 2 * 1024;               // one window of one 32-row tile
+  static constexpr int SCALE_LDS = WT == W_MXFP4 ? W * 2 * R * WIN : 0;
+  static constexpr int LDS = D * BUF + SCALE_LDS;
   // token-row pieces of 1 KB per wave per chunk for NT tiles, spread over the
   // waves (a wave past the last piece re-loads it)
   template <int NT>
@@ -78,9 +87,10 @@ struct GConf {
   static constexpr int scale_pieces_total() { return NATIVE ? (NT + 1) / 2 : 0; }
   template <int NT>
   static constexpr int scale_pieces() { return (scale_pieces_total<NT>() + W - 1) / W; }
-  // vector loads per wave per chunk
+  // vector loads per wave per chunk (besides the weight-scale windows' loads,
+  // which only some chunks issue)
   template <int NT>
-  static constexpr int loads() { return pieces<NT>() + R * (LPT + SPT) + scale_pieces<NT>(); }
+  static constexpr int loads() { return pieces<NT>() + R * LPT + scale_pieces<NT>(); }
   // position of piece p of token row r inside the row: the rows one 128-bit LDS read
   // touches land in distinct bank groups whether it is served 8 or 16 lanes at a time
   static __device__ __forceinline__ int swz(int r) {
@@ -98,7 +108,8 @@ using PrefillConf = GConf<WT, WT == W_MXFP4 ? 8 : 4, 2, 4, 4>;
 // tokens streams its weights once.
 using NativeConf = GConf<W_MXFP4, 4, 2, 5, 8, true>;
 
-// One ring slot of weight registers: the wave's R row tiles for one chunk.
+// One ring slot of weight registers: the wave's R row tiles for one chunk
+// (MXFP4: sw[t] the E8M0 scale of the lane's 32-column block, read from LDS).
 template <typename CF>
 struct GA {
   u32x4 code[CF::R][CF::LPT];
@@ -133,7 +144,7 @@ __device__ __forceinline__ void g_dma4(__amdgpu_buffer_rsrc_t src, int voff, int
 // uniform part, tile and column step, goes into the scalar offset).
 struct GLane {
   int code_voff;   // lane's fragment inside the (tile, step) pair it reads
-  int scale_voff;  // MXFP4: lane's bytes inside the scale block pair
+  int scale_off;   // MXFP4: lane's scale bytes inside its tile's LDS window
 };
 
 template <typename CF>
@@ -143,15 +154,12 @@ __device__ __forceinline__ void g_issue_weights(GA<CF>& a, const Mat& w, const G
 #pragma unroll
   for (int t = 0; t < R; ++t) {
     if constexpr (WT == W_MXFP4) {
-      const int s = c >> 1;  // 128-column step holding the chunk
-      a.code[t][0] = bld16(w.codes, ln.code_voff, (st0[t] * w.nK + s) * 1024 + (c & 1) * 512);
-      a.sw[t] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-          w.scales, ln.scale_voff, (st0[t] * w.nKs + (s >> 4)) * 1024 + (c & 1) * 512 + ((s & 15) >> 2) * 4, 0);
+      // 128-column step c / 2, its half c % 2
+      a.code[t][0] = bld16(w.codes, ln.code_voff, (st0[t] * w.nK + (c >> 1)) * 1024 + (c & 1) * 512);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)  // k-step j of the chunk: 32-column step 2c + j / 2, half j % 2
         a.code[t][j] = bld16(w.codes, ln.code_voff, (st0[t] * w.nK + 2 * c + (j >> 1)) * 1024 + (j & 1) * 512);
-      a.sw[t] = 0u;
     }
   }
 }
@@ -168,9 +176,8 @@ __device__ __forceinline__ void g_compute(const GA<CF>& a, const uint8_t* buf, i
   const int h = (threadIdx.x & 63) >> 5;
   float sc[R];
   if constexpr (WT == W_MXFP4) {
-    const int sh = 8 * ((c >> 1) & 3);
 #pragma unroll
-    for (int t = 0; t < R; ++t) sc[t] = e8m0_to_f32((a.sw[t] >> sh) & 0xffu);
+    for (int t = 0; t < R; ++t) sc[t] = e8m0_to_f32(a.sw[t]);
   }
   bf16x8 B[2][NT], A[2][R];
   auto operands = [&](int m, bf16x8 (&b)[NT], bf16x8 (&aa)[R]) {
@@ -234,14 +241,14 @@ __device__ __forceinline__ void g_mma_native(const GA<CF>& a, int c, const uint8
                                              f32x16 (&acc)[CF::R][NT]) {
   constexpr int R = CF::R;
   const int h = (threadIdx.x & 63) >> 5;
-  const int sha = 8 * ((c >> 1) & 3), shb = 8 * (2 * (c & 1) + h);
+  const int shb = 8 * (2 * (c & 1) + h);
   i32x8 A[R];
   int sa[R];
 #pragma unroll
   for (int t = 0; t < R; ++t) {
     const u32x4 q = a.code[t][0];
     A[t] = i32x8{(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
-    sa[t] = (int)(a.sw[t] >> sha);
+    sa[t] = (int)a.sw[t];
   }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -273,7 +280,7 @@ __device__ __forceinline__ void g_pass(const Mat& w, const TileOf& tile_of, __am
   const int rho = lane & 31, h = lane >> 5;
   GLane ln;
   ln.code_voff = (rho >> 4) * w.nK * 1024 + (rho & 15) * 16 + h * 256;
-  ln.scale_voff = WT == W_MXFP4 ? (rho >> 4) * w.nKs * 1024 + (rho & 15) * 16 + h * 256 : 0;
+  ln.scale_off = (rho >> 4) * 1024 + h * 256 + (rho & 15) * 16;
   int st0[R];
 #pragma unroll
   for (int t = 0; t < R; ++t) st0[t] = 2 * tile_of(t);
@@ -315,6 +322,41 @@ __device__ __forceinline__ void g_pass(const Mat& w, const TileOf& tile_of, __am
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[t][nt][v] = 0.0f;
+  // MXFP4 weight scales: window v (chunks 32 v .. 32 v + 31) of the wave's row
+  // tiles goes to LDS set v % 2 with one 1 KB load per 16-row tile.  Window v + 1
+  // is loaded at the top of the first loop round that starts at chunk 32 v + 8 or
+  // later (before that round's loads, at most D - 1 chunks later), so it replaces
+  // window v - 1 after that window's last read (chunk 32 v - 1, read during step
+  // 32 v - 2) and has landed with the round's first chunk, long before its own
+  // first read (step 32 v + 31).  Only this wave reads its windows, so its own
+  // vmcnt waits order them.  The loads sit outside the unrolled steps: a branch
+  // inside them costs the native kernel a great many spills.
+  uint8_t* const wsc = lds + D * CF::BUF + wv * 2 * R * CF::WIN;
+  auto issue_scales = [&](int v) {
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        g_dma16(w.scales, 16 * lane, ((st0[t] + q) * w.nKs + v) * 1024, wsc + ((v & 1) * R + t) * CF::WIN + q * 1024);
+  };
+  // the scale bytes of chunk c into ring slot g (step c / 2 within its window)
+  auto read_scales = [&](GA<CF>& g, int c) {
+    if constexpr (WT == W_MXFP4) {
+      const uint8_t* p = wsc + ((c >> 5) & 1) * R * CF::WIN + (c & 1) * 512 + ((c >> 1) & 15) + ln.scale_off;
+#pragma unroll
+      for (int t = 0; t < R; ++t) g.sw[t] = p[t * CF::WIN];
+    }
+  };
+  int next_win = 1;
+  auto round_scales = [&](int c0) {
+    if constexpr (WT == W_MXFP4) {
+      if (next_win < w.nKs && c0 + 24 >= 32 * next_win) {
+        issue_scales(next_win);
+        ++next_win;
+      }
+    }
+  };
+  // chunk c's loads into ring slot `slot` (past the end the last chunk is re-loaded)
   auto issue = [&](int slot, int c) {
 #pragma unroll
     for (int i = 0; i < PW; ++i)
@@ -329,7 +371,10 @@ __device__ __forceinline__ void g_pass(const Mat& w, const TileOf& tile_of, __am
     }
   };
   // The prologue's chunks are kept apart (and in order) like the loop's, so that
-  // the waits below count the same loads.
+  // the waits below count the same loads.  Window 0 goes first: it has landed once
+  // chunk 0 has.  The windows' loads come on top of some chunks' NL, which only
+  // makes the waits below (at most so many loads outstanding) wait a little longer.
+  if constexpr (WT == W_MXFP4) issue_scales(0);
 #pragma unroll
   for (int d = 0; d < D - 1; ++d) {
     issue(d, min(d, nch - 1));
@@ -347,13 +392,17 @@ __device__ __forceinline__ void g_pass(const Mat& w, const TileOf& tile_of, __am
     uint32_t bsw[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) g_read_native<CF>(lds, nt, brow[nt], bswz[nt], B[nt], bsw[nt]);
+    read_scales(a[0], 0);
+    // step c also reads chunk c+1's weight scales (its window landed long before)
     auto step = [&](int d, int c) {
       issue((d + D - 1) % D, min(c + D - 1, nch - 1));
+      read_scales(a[(d + 1) % D], min(c + 1, nch - 1));
       __builtin_amdgcn_sched_barrier(0);
       g_mma_native<CF, NT>(a[d], c, lds + ((d + 1) % D) * CF::BUF, brow, bswz, B, bsw, acc);
       g_wait_barrier<(D - 3) * NL>();
     };
     for (; c0 + D <= nch; c0 += D) {
+      round_scales(c0);
 #pragma unroll
       for (int d = 0; d < D; ++d) step(d, c0 + d);
     }
@@ -364,12 +413,15 @@ __device__ __forceinline__ void g_pass(const Mat& w, const TileOf& tile_of, __am
   } else {
     // step c ends with chunk c+1 in LDS: D - 2 chunks may stay in flight
     g_wait_barrier<(D - 2) * NL>();
+    read_scales(a[0], 0);
     auto step = [&](int d, int c) {
       issue((d + D - 1) % D, min(c + D - 1, nch - 1));
+      read_scales(a[(d + 1) % D], min(c + 1, nch - 1));
       g_compute<CF, NT>(a[d], lds + d * CF::BUF, c, brow, bswz, acc);
       g_wait_barrier<(D - 2) * NL>();
     };
     for (; c0 + D <= nch; c0 += D) {
+      round_scales(c0);
 #pragma unroll
       for (int d = 0; d < D; ++d) step(d, c0 + d);
     }
@@ -433,7 +485,7 @@ __global__ __launch_bounds__(CF::W * 64) __attribute__((amdgpu_waves_per_eu(CF::
     FfnArgs a, GGrid gr) {
   const Item it = resolve_item_at(a, xcd_logical_block(), gr.shared_blocks, gr.routed_blocks);
   if (!it.valid) return;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[CF::D * CF::BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[CF::LDS];
   constexpr int R = CF::R, WT = CF::WT;
   const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
   const int j = lane & 31, h = lane >> 5;
@@ -478,7 +530,7 @@ __global__ __launch_bounds__(CF::W * 64) __attribute__((amdgpu_waves_per_eu(CF::
     FfnArgs a, GGrid gr) {
   const Item it = resolve_item_at(a, xcd_logical_block(), gr.shared_blocks, gr.routed_blocks);
   if (!it.valid) return;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[CF::D * CF::BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[CF::LDS];
   constexpr int R = CF::R, WT = CF::WT;
   const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
   const int j = lane & 31, h = lane >> 5;

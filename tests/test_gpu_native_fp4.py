@@ -91,6 +91,10 @@ NATIVE_CASES = [
     (700, 256, 128, 2, 1, False, "normal"),
     (220, 4096, 256, 8, 2, False, "zipf"),
     (600, 1024, 384, 16, 4, True, "zipf"),
+    # weight-scale windows of 2048 columns: four for K = 8192, a short second one
+    # for K = 2176 (gate_up) and 2304 (down)
+    (300, 8192, 256, 4, 2, False, "normal"),
+    (140, 2176, 2304, 4, 2, True, "zipf"),
 ]
 
 

@@ -178,6 +178,11 @@ SMALL = [
     (synth.MXFP4, 400, 4096, 256, 8, 2, False, "normal", "G"),
     (synth.MXFP4, 220, 4096, 256, 8, 2, True, "zipf", "G"),
     (synth.BF16, 300, 4096, 256, 8, 2, False, "zipf", "G"),
+    # MXFP4 weight scales staged in LDS 32 chunks (2048 columns) at a time, two
+    # windows alternating: gate_up K = 8192 (four windows, each set refilled), and
+    # K = 2176 / 2304 (a second window of 2 and 4 chunks), shared down K = 1152
+    (synth.MXFP4, 300, 8192, 256, 8, 2, False, "normal", "G"),
+    (synth.MXFP4, 140, 2176, 2304, 4, 2, True, "zipf", "G"),
     # MXFP4 weight streaming with whole 16-step scale blocks (K = 2048): one and two
     # token tiles, a shared expert whose down K (1024) is half a block, and a
     # Zipf-skewed batch whose hottest expert carries 98 tokens (several passes)
