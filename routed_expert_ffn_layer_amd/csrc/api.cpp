@@ -270,6 +270,7 @@ int grouped_ffn(int phases, int wdt, const void* slot_pool, size_t slot_stride, 
   a.I_shared = I_shared;
   a.h_ld = I > I_shared ? I : I_shared;
   a.routed_items = (int)((int64_t)T * k < E ? (int64_t)T * k : E);
+  a.pass_rows = 0;  // one item per expert (the decode launchers split items into passes)
   a.lds_rows = 0;  // set per launch by the decode launchers
   a.xq = nullptr;
   a.xs = nullptr;

@@ -35,7 +35,9 @@ struct FfnArgs {
   void* h;                        // workspace: [T*k + T][I_max] bf16 or f32
   int T, k, E, H, I, I_shared;
   int h_ld;                       // row stride of h in elements (max(I, I_shared))
-  int routed_items;               // grid slots for routed experts: min(E, T*k)
+  int routed_items;               // grid slots for routed items (an upper bound on their number)
+  int pass_rows;                  // a power of two: an item is a run of up to pass_rows pairs of one
+                                  // expert (the shared expert: of its tokens); 0: one item per expert
   int lds_rows;                   // token rows the launch's dynamic LDS holds (0: none)
 };
 
@@ -111,14 +113,18 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Item resolution for the grouped FFN.  The a-th expert (ascending id) that has
-// pairs and a slot (or a non-zero weight address) in this call.  Every lane of the wave gets the same answer.
-// Returns -1 if fewer than a+1 experts are active.  All loads are issued before
-// the scan, so the lookup costs one memory round trip.
-template <int EPL>
-__device__ __forceinline__ int nth_active_expert_t(const int32_t* __restrict__ offsets,
-                                                   const int32_t* __restrict__ slot_of_expert,
-                                                   const uint64_t* __restrict__ expert_addr, int E, int a) {
+// Item resolution for the grouped FFN.  Items are taken in ascending expert id over
+// the experts that have pairs and a slot (or a non-zero weight address) in this call:
+// one item per expert (P = 0), or one item per run of up to P of its pairs (P > 0:
+// an expert with n pairs gives ceil(n / P) items, so the passes of a busy expert run
+// on different waves side by side).  Returns the expert of item a and, in *run, the
+// item's index among that expert's items (P is 0 or a power of two); every lane of the
+// wave gets the same answer;
+// -1 if there are fewer than a+1 items.  All loads are issued before the scan, so the
+// lookup costs one memory round trip.
+template <int EPL, bool RUNS>
+__device__ __forceinline__ int nth_item_t(const int32_t* __restrict__ offsets, const int32_t* __restrict__ slot_of_expert,
+                                          const uint64_t* __restrict__ expert_addr, int E, int a, int P, int* run) {
   const int lane = threadIdx.x & 63;
   int lo[EPL], hi[EPL], sl[EPL];
 #pragma unroll
@@ -132,29 +138,41 @@ __device__ __forceinline__ int nth_active_expert_t(const int32_t* __restrict__ o
     else
       sl[i] = in ? slot_of_expert[e] : -1;
   }
+  const int lp = P > 0 ? __builtin_ctz((unsigned)P) : 0;
   int base = 0;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const int act = (hi[i] > lo[i]) && (sl[i] >= 0);
-    const int incl = wave_incl_scan(act);
+    const int n = hi[i] - lo[i];
+    const int cnt = (n > 0 && sl[i] >= 0) ? (RUNS && P > 0 ? (n + P - 1) >> lp : 1) : 0;
+    const int incl = wave_incl_scan(cnt);
     const int total = __shfl(incl, 63, 64);
     if (a < base + total) {
-      const uint64_t hit = __ballot(act && (incl == a + 1 - base));
-      return i * 64 + __builtin_ctzll(hit);
+      const int r = a - base;  // item r of this group of 64 experts
+      if constexpr (RUNS) {
+        const uint64_t hit = __ballot(cnt > 0 && incl > r && incl - cnt <= r);
+        const int owner = __builtin_ctzll(hit);
+        *run = r - __shfl(incl - cnt, owner, 64);
+        return i * 64 + owner;
+      } else {
+        *run = 0;
+        return i * 64 + __builtin_ctzll(__ballot(cnt && incl == r + 1));
+      }
     }
     base += total;
   }
+  *run = 0;
   return -1;
 }
 
-__device__ __forceinline__ int nth_active_expert(const int32_t* __restrict__ offsets,
-                                                 const int32_t* __restrict__ slot_of_expert,
-                                                 const uint64_t* __restrict__ expert_addr, int E, int a) {
-  if (E <= 64) return nth_active_expert_t<1>(offsets, slot_of_expert, expert_addr, E, a);
-  if (E <= 128) return nth_active_expert_t<2>(offsets, slot_of_expert, expert_addr, E, a);
-  if (E <= 256) return nth_active_expert_t<4>(offsets, slot_of_expert, expert_addr, E, a);
-  if (E <= 512) return nth_active_expert_t<8>(offsets, slot_of_expert, expert_addr, E, a);
-  return nth_active_expert_t<16>(offsets, slot_of_expert, expert_addr, E, a);
+// RUNS false: P is taken as 0 (one item per expert), compiled without the run count.
+template <bool RUNS>
+__device__ __forceinline__ int nth_item(const int32_t* __restrict__ offsets, const int32_t* __restrict__ slot_of_expert,
+                                        const uint64_t* __restrict__ expert_addr, int E, int a, int P, int* run) {
+  if (E <= 64) return nth_item_t<1, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P, run);
+  if (E <= 128) return nth_item_t<2, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P, run);
+  if (E <= 256) return nth_item_t<4, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P, run);
+  if (E <= 512) return nth_item_t<8, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P, run);
+  return nth_item_t<16, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P, run);
 }
 
 }  // namespace moe

@@ -8,11 +8,12 @@
 // (SwiGLU: down(SiLU(gate x) * up x)) is not on the pages; it is the standard
 // MoE expert.
 //
-// Work decomposition.  A grid slot is (item, tile).  Items are the shared expert
-// (if any) followed by up to min(E, T*k) routed experts; a block finds "its"
-// routed expert as the a-th expert with pairs and a slot (a scan over offsets in
-// L2), so the grid is sized from T alone and needs no host synchronisation.
-// Weights are streamed from HBM exactly once per expert (per 16*NT tokens).
+// Work decomposition.  A grid slot is (item, tile).  An item is one pass (up to
+// 16*NT tokens) of one expert: the shared expert's passes (if any) come first, then
+// the passes of the routed experts in ascending id; a block finds "its" item by a
+// scan over the offsets (in L2), so the grid is sized from T alone (an upper bound
+// on the items) and needs no host synchronisation.  Each pass streams its expert's
+// weights once; the passes of one expert run side by side.
 // The KW waves of a K split add their partial accumulators in a fixed order, so
 // results are deterministic run to run.  Block shapes (waves, K split, row tiles
 // per wave, token tiles per pass) are chosen per weight type and batch by the
@@ -403,7 +404,7 @@ __global__ __launch_bounds__((64 * dec_wpb<WT, NT>())) __attribute__((amdgpu_wav
     FfnArgs a, int shared_tiles, int routed_tiles) {
   constexpr int RT = dec_wpb<WT, NT>() / KW;
   static_assert(RT >= 1, "waves per block split by KW");
-  const Item it = resolve_item(a, shared_tiles, routed_tiles);
+  const Item it = resolve_item<(NT > 1)>(a, shared_tiles, routed_tiles);  // one-tile passes never split
   if (!it.valid) return;
   __shared__ f32x4 red[KW > 1 ? dec_wpb<WT, NT>() : 1][R][NT][64];
   const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
@@ -432,7 +433,7 @@ __global__ __launch_bounds__((64 * dec_wpb<WT, NT>())) __attribute__((amdgpu_wav
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int i = min(pass + nt * 16 + r, it.n - 1);  // padding columns re-read a real row
-      xrow[nt] = item_token(a, it, i);
+      xrow[nt] = item_token<(NT > 1)>(a, it, i);
     }
     bool staged = false;  // uniform per block: this pass's token rows are in LDS
     if constexpr (LB) {
@@ -442,7 +443,7 @@ __global__ __launch_bounds__((64 * dec_wpb<WT, NT>())) __attribute__((amdgpu_wav
       if (pass > 0) __syncthreads();  // the previous pass has finished reading
       if (staged)
         stage_rows(lds_rows, reinterpret_cast<const uint16_t*>(a.x), np, H,
-                   [&](int i) { return (size_t)item_token(a, it, pass + i) * H; });
+                   [&](int i) { return (size_t)item_token<(NT > 1)>(a, it, pass + i) * H; });
       __syncthreads();
       if (staged) {
         rows.lds = lds_rows;
@@ -525,7 +526,7 @@ __global__ __launch_bounds__((64 * dec_wpb<WT, NT>())) __attribute__((amdgpu_wav
     FfnArgs a, int shared_tiles, int routed_tiles) {
   constexpr int RT = dec_wpb<WT, NT>() / KW;
   static_assert(RT >= 1, "waves per block split by KW");
-  const Item it = resolve_item(a, shared_tiles, routed_tiles);
+  const Item it = resolve_item<(NT > 1)>(a, shared_tiles, routed_tiles);  // one-tile passes never split
   if (!it.valid) return;
   __shared__ f32x4 red[KW > 1 ? dec_wpb<WT, NT>() : 1][R][NT][64];
   const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
@@ -618,7 +619,7 @@ __global__ __launch_bounds__((64 * dec_wpb<WT, NT>())) __attribute__((amdgpu_wav
               for (int q = 1; q < KW; ++q) v += red[wv + q][t][nt][lane];
               const int i = pass + nt * 16 + r;
               if (i < it.n) {
-                float* dst = it.shared ? a.shared_out + (size_t)i * H : a.out_rows + (size_t)(it.p0 + i) * H;
+                float* dst = it.shared ? a.shared_out + (size_t)((NT > 1 ? it.p0 : 0) + i) * H : a.out_rows + (size_t)(it.p0 + i) * H;
                 *reinterpret_cast<float4*>(dst + row0 + 16 * t + g * 4) = make_float4(v[0], v[1], v[2], v[3]);
               }
             }
@@ -671,6 +672,23 @@ constexpr int kDecMxNtMax = 2;  // MXFP4: token tiles per pass
 static int pick_nt(int T, int wtype) {
   const int nt = T <= 16 ? 1 : T <= 32 ? 2 : T <= 64 ? 4 : 8;
   return wtype == W_MXFP4 && nt > kDecMxNtMax ? kDecMxNtMax : nt;
+}
+
+// Work items of the MFMA decode kernels are single passes: an expert with more pairs
+// than one pass holds gives one item per pass, so its passes run on different waves
+// at the same time (the waves of an item's passes stream the same weights, which the
+// block order puts on one XCD, and each wave's work is at most one pass: a busy
+// expert's second pass no longer decides when the launch ends).
+static FfnArgs pass_split(const FfnArgs& a, int wtype) {
+  FfnArgs b = a;
+  const int P = 16 * pick_nt(a.T, wtype);  // a power of two
+  // else no expert has more pairs than one pass holds (at most T); in particular the
+  // one-tile kernels (T <= 16), compiled without the split, always get 0
+  if (P < a.T) {
+    b.pass_rows = P;
+    b.routed_items = routed_item_bound(a.T, a.k, a.E, P);
+  }
+  return b;
 }
 
 // MXFP4 passes of one token tile take their token rows from LDS (staged once per
@@ -731,17 +749,18 @@ hipError_t launch_ffn_gate_up(int wtype, const FfnArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   const Shape sp = gate_up_shape(wtype, a.T);
+  const FfnArgs b = pass_split(a, wtype);
   const int rb = 8 * sp.r * (dec_wpb_of(wtype, pick_nt(a.T, wtype)) / sp.kw);  // intermediate indices per block
   const int shared_tiles = sh ? (a.I_shared + rb - 1) / rb : 0, routed_tiles = (a.I + rb - 1) / rb;
-  const unsigned grid = shared_tiles + a.routed_items * routed_tiles;
+  const unsigned grid = shared_tiles * shared_items(a.T, b.pass_rows) + b.routed_items * routed_tiles;
   if (!grid) return hipSuccess;
   if (wtype == W_BF16) {
-    if (sp.kw == 4) gu_nt<W_BF16, 4, 1>(a, st, grid, shared_tiles, routed_tiles);
-    else gu_nt<W_BF16, 2, 1>(a, st, grid, shared_tiles, routed_tiles);
+    if (sp.kw == 4) gu_nt<W_BF16, 4, 1>(b, st, grid, shared_tiles, routed_tiles);
+    else gu_nt<W_BF16, 2, 1>(b, st, grid, shared_tiles, routed_tiles);
   } else {
-    if (sp.r == 1) gu_nt<W_MXFP4, 1, 1>(a, st, grid, shared_tiles, routed_tiles);
-    else if (sp.r == 2) gu_nt<W_MXFP4, 1, 2>(a, st, grid, shared_tiles, routed_tiles);
-    else gu_nt<W_MXFP4, 1, 4>(a, st, grid, shared_tiles, routed_tiles);
+    if (sp.r == 1) gu_nt<W_MXFP4, 1, 1>(b, st, grid, shared_tiles, routed_tiles);
+    else if (sp.r == 2) gu_nt<W_MXFP4, 1, 2>(b, st, grid, shared_tiles, routed_tiles);
+    else gu_nt<W_MXFP4, 1, 4>(b, st, grid, shared_tiles, routed_tiles);
   }
   return hipGetLastError();
 }
@@ -757,15 +776,16 @@ hipError_t launch_ffn_down(int wtype, const FfnArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   const Shape sp = down_shape(wtype, a.T);
+  const FfnArgs b = pass_split(a, wtype);
   const int rb = 16 * sp.r * (dec_wpb_of(wtype, pick_nt(a.T, wtype)) / sp.kw);  // output columns per block
   const int tiles = (a.H + rb - 1) / rb;
   const int shared_tiles = sh ? tiles : 0;
-  const unsigned grid = shared_tiles + a.routed_items * tiles;
+  const unsigned grid = shared_tiles * shared_items(a.T, b.pass_rows) + b.routed_items * tiles;
   if (!grid) return hipSuccess;
-  if (wtype == W_BF16) dn_nt<W_BF16, kDecBf16DnKw, kDecBf16DnR>(a, st, grid, shared_tiles, tiles);
-  else if (sp.r == 1) dn_nt<W_MXFP4, 1, 1>(a, st, grid, shared_tiles, tiles);
-  else if (sp.r == 2) dn_nt<W_MXFP4, 1, 2>(a, st, grid, shared_tiles, tiles);
-  else dn_nt<W_MXFP4, 1, 4>(a, st, grid, shared_tiles, tiles);
+  if (wtype == W_BF16) dn_nt<W_BF16, kDecBf16DnKw, kDecBf16DnR>(b, st, grid, shared_tiles, tiles);
+  else if (sp.r == 1) dn_nt<W_MXFP4, 1, 1>(b, st, grid, shared_tiles, tiles);
+  else if (sp.r == 2) dn_nt<W_MXFP4, 1, 2>(b, st, grid, shared_tiles, tiles);
+  else dn_nt<W_MXFP4, 1, 4>(b, st, grid, shared_tiles, tiles);
   return hipGetLastError();
 }
 

@@ -11,33 +11,58 @@ struct Item {
   const uint8_t* w;  // expert slot
   int I;             // intermediate size
   int n;             // tokens of the item
-  int p0;            // first output row (routed: sorted position; shared: 0)
+  int p0;            // first pair of the item in sorted order (shared: first token)
   int hrow0;         // first row of the item in the intermediate workspace
   int tile;          // tile index inside the item
   bool shared;
   bool valid;
 };
 
-// Work item of logical block b: the shared expert's tiles come first, then
-// routed_tiles tiles of each active routed expert in ascending expert id.
+// Items of the shared expert: its T tokens in runs of up to P (one item if P = 0;
+// P is 0 or a power of two).
+__host__ __device__ inline int shared_items(int T, int P) { return P > 0 ? (T + P - 1) >> __builtin_ctz((unsigned)P) : 1; }
+
+// Upper bound on the routed items of a call: N = T*k pairs over at most
+// A = min(E, N) experts, each expert's ceil(n / P) <= (n + P - 1) / P, summed.
+inline int routed_item_bound(int T, int k, int E, int P) {
+  const int64_t N = (int64_t)T * k, A = N < E ? N : E;
+  return (int)(P > 0 ? (N + A * (P - 1)) / P : A);
+}
+
+// Work item of logical block b: the shared expert's items come first (shared_tiles
+// blocks each), then routed_tiles blocks of each routed item in ascending expert id
+// (and, within an expert, ascending run).  An item covers pairs p0 .. p0+n-1 of the
+// sorted order (the shared expert: tokens p0 .. p0+n-1).  Kernels that never split
+// (SPLIT false: a.pass_rows is 0 for them) compile the one-item-per-expert lookup.
+template <bool SPLIT = false>
 __device__ __forceinline__ Item resolve_item_at(const FfnArgs& a, int b, int shared_tiles, int routed_tiles) {
   Item it;
-  if (b < shared_tiles) {
+  const int P = SPLIT ? a.pass_rows : 0;
+  const int shared_total = SPLIT && a.shared_w ? shared_tiles * shared_items(a.T, P) : shared_tiles;
+  if (b < shared_total) {
     it.shared = true;
     it.valid = true;
     it.w = a.shared_w;
     it.I = a.I_shared;
-    it.n = a.T;
-    it.p0 = 0;
-    it.hrow0 = a.T * a.k;
-    it.tile = b;
+    if (SPLIT && P > 0) {
+      const int run = b / shared_tiles;
+      it.p0 = run * P;
+      it.n = min(P, a.T - it.p0);
+      it.tile = b - run * shared_tiles;
+    } else {
+      it.p0 = 0;
+      it.n = a.T;
+      it.tile = b;
+    }
+    it.hrow0 = a.T * a.k + it.p0;
     return it;
   }
-  b -= shared_tiles;
+  b -= shared_total;
   const int item = b / routed_tiles;
   it.tile = b - item * routed_tiles;
   it.shared = false;
-  const int e = uniform(nth_active_expert(a.offsets, a.slot_of_expert, a.expert_addr, a.E, item));
+  int run = 0;
+  const int e = uniform(nth_item<SPLIT>(a.offsets, a.slot_of_expert, a.expert_addr, a.E, item, P, &run));
   it.valid = e >= 0;
   if (!it.valid) return it;
   it.w = a.expert_addr ? uniform(reinterpret_cast<const uint8_t*>(a.expert_addr[e]))
@@ -45,16 +70,25 @@ __device__ __forceinline__ Item resolve_item_at(const FfnArgs& a, int b, int sha
   it.I = a.I;
   it.p0 = uniform(a.offsets[e]);
   it.n = uniform(a.offsets[e + 1]) - it.p0;
+  if (SPLIT && P > 0) {
+    const int skip = uniform(run) * P;
+    it.p0 += skip;
+    it.n = min(P, it.n - skip);
+  }
   it.hrow0 = it.p0;
   return it;
 }
 
+template <bool SPLIT = false>
 __device__ __forceinline__ Item resolve_item(const FfnArgs& a, int shared_tiles, int routed_tiles) {
-  return resolve_item_at(a, blockIdx.x, shared_tiles, routed_tiles);
+  return resolve_item_at<SPLIT>(a, blockIdx.x, shared_tiles, routed_tiles);
 }
 
+// Token of row i of an item (SPLIT as for the lookup: only then does a shared item
+// start past token 0).
+template <bool SPLIT = false>
 __device__ __forceinline__ int item_token(const FfnArgs& a, const Item& it, int i) {
-  return it.shared ? i : a.sorted_rows[it.p0 + i] / a.k;
+  return it.shared ? (SPLIT ? it.p0 + i : i) : a.sorted_rows[it.p0 + i] / a.k;
 }
 
 template <int WT>
