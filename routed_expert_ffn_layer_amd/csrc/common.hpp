@@ -115,30 +115,42 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 // Item resolution for the grouped FFN.  Items are taken in ascending expert id over
 // the experts that have pairs and a slot (or a non-zero weight address) in this call:
-// one item per expert (P = 0), or one item per run of up to P of its pairs (P > 0:
-// an expert with n pairs gives ceil(n / P) items, so the passes of a busy expert run
-// on different waves side by side).  Returns the expert of item a and, in *run, the
-// item's index among that expert's items (P is 0 or a power of two); every lane of the
-// wave gets the same answer;
-// -1 if there are fewer than a+1 items.  All loads are issued before the scan, so the
-// lookup costs one memory round trip.
+// one item per expert (RUNS false), or one item per run of up to P of its pairs (RUNS,
+// P > 0, a power of two: an expert with n pairs gives ceil(n / P) items, so the passes
+// of a busy expert run on different waves side by side).  Finds item a: its expert,
+// the item's index among that expert's items, and the expert's first and end pair
+// and slot or weight address, taken from the lane that loaded them (no second trip
+// to memory).  Every lane of the wave gets the same answer; expert -1 if there are
+// fewer than a+1 items.  All loads are issued before the scan, so the lookup costs
+// one memory round trip.
+struct ItemRef {
+  int expert, run, lo, hi, slot;
+  uint64_t addr;
+};
+
 template <int EPL, bool RUNS>
-__device__ __forceinline__ int nth_item_t(const int32_t* __restrict__ offsets, const int32_t* __restrict__ slot_of_expert,
-                                          const uint64_t* __restrict__ expert_addr, int E, int a, int P, int* run) {
+__device__ __forceinline__ ItemRef nth_item_t(const int32_t* __restrict__ offsets,
+                                              const int32_t* __restrict__ slot_of_expert,
+                                              const uint64_t* __restrict__ expert_addr, int E, int a, int P) {
   const int lane = threadIdx.x & 63;
   int lo[EPL], hi[EPL], sl[EPL];
+  uint64_t ad[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = i * 64 + lane;
     const bool in = e < E;
     lo[i] = in ? offsets[e] : 0;
     hi[i] = in ? offsets[e + 1] : 0;
-    if (expert_addr)
-      sl[i] = in && expert_addr[e] != 0 ? 0 : -1;
-    else
+    ad[i] = 0;
+    if (expert_addr) {
+      ad[i] = in ? expert_addr[e] : 0;
+      sl[i] = ad[i] != 0 ? 0 : -1;
+    } else {
       sl[i] = in ? slot_of_expert[e] : -1;
+    }
   }
-  const int lp = P > 0 ? __builtin_ctz((unsigned)P) : 0;
+  const int lp = RUNS && P > 0 ? __builtin_ctz((unsigned)P) : 0;
+  ItemRef ref;
   int base = 0;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
@@ -148,31 +160,39 @@ __device__ __forceinline__ int nth_item_t(const int32_t* __restrict__ offsets, c
     const int total = __shfl(incl, 63, 64);
     if (a < base + total) {
       const int r = a - base;  // item r of this group of 64 experts
+      int owner;
       if constexpr (RUNS) {
-        const uint64_t hit = __ballot(cnt > 0 && incl > r && incl - cnt <= r);
-        const int owner = __builtin_ctzll(hit);
-        *run = r - __shfl(incl - cnt, owner, 64);
-        return i * 64 + owner;
+        owner = __builtin_ctzll(__ballot(cnt > 0 && incl > r && incl - cnt <= r));
+        ref.run = r - __shfl(incl - cnt, owner, 64);
       } else {
-        *run = 0;
-        return i * 64 + __builtin_ctzll(__ballot(cnt && incl == r + 1));
+        owner = __builtin_ctzll(__ballot(cnt && incl == r + 1));
+        ref.run = 0;
       }
+      ref.expert = i * 64 + owner;
+      ref.lo = __shfl(lo[i], owner, 64);
+      ref.hi = __shfl(hi[i], owner, 64);
+      ref.slot = __shfl(sl[i], owner, 64);
+      ref.addr = expert_addr ? ((uint64_t)(uint32_t)__shfl((int)(uint32_t)(ad[i] >> 32), owner, 64) << 32) |
+                                   (uint32_t)__shfl((int)(uint32_t)ad[i], owner, 64)
+                             : 0;
+      return ref;
     }
     base += total;
   }
-  *run = 0;
-  return -1;
+  ref.expert = -1;
+  ref.run = ref.lo = ref.hi = ref.slot = 0;
+  ref.addr = 0;
+  return ref;
 }
 
-// RUNS false: P is taken as 0 (one item per expert), compiled without the run count.
 template <bool RUNS>
-__device__ __forceinline__ int nth_item(const int32_t* __restrict__ offsets, const int32_t* __restrict__ slot_of_expert,
-                                        const uint64_t* __restrict__ expert_addr, int E, int a, int P, int* run) {
-  if (E <= 64) return nth_item_t<1, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P, run);
-  if (E <= 128) return nth_item_t<2, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P, run);
-  if (E <= 256) return nth_item_t<4, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P, run);
-  if (E <= 512) return nth_item_t<8, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P, run);
-  return nth_item_t<16, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P, run);
+__device__ __forceinline__ ItemRef nth_item(const int32_t* __restrict__ offsets, const int32_t* __restrict__ slot_of_expert,
+                                            const uint64_t* __restrict__ expert_addr, int E, int a, int P) {
+  if (E <= 64) return nth_item_t<1, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P);
+  if (E <= 128) return nth_item_t<2, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P);
+  if (E <= 256) return nth_item_t<4, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P);
+  if (E <= 512) return nth_item_t<8, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P);
+  return nth_item_t<16, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P);
 }
 
 }  // namespace moe

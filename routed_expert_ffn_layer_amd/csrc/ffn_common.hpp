@@ -61,17 +61,16 @@ __device__ __forceinline__ Item resolve_item_at(const FfnArgs& a, int b, int sha
   const int item = b / routed_tiles;
   it.tile = b - item * routed_tiles;
   it.shared = false;
-  int run = 0;
-  const int e = uniform(nth_item<SPLIT>(a.offsets, a.slot_of_expert, a.expert_addr, a.E, item, P, &run));
-  it.valid = e >= 0;
+  const ItemRef ref = nth_item<SPLIT>(a.offsets, a.slot_of_expert, a.expert_addr, a.E, item, P);
+  it.valid = uniform(ref.expert) >= 0;
   if (!it.valid) return it;
-  it.w = a.expert_addr ? uniform(reinterpret_cast<const uint8_t*>(a.expert_addr[e]))
-                       : uniform(a.slot_pool + (uint64_t)uniform(a.slot_of_expert[e]) * a.slot_stride);
+  it.w = a.expert_addr ? uniform(reinterpret_cast<const uint8_t*>(ref.addr))
+                       : uniform(a.slot_pool + (uint64_t)uniform(ref.slot) * a.slot_stride);
   it.I = a.I;
-  it.p0 = uniform(a.offsets[e]);
-  it.n = uniform(a.offsets[e + 1]) - it.p0;
+  it.p0 = uniform(ref.lo);
+  it.n = uniform(ref.hi) - it.p0;
   if (SPLIT && P > 0) {
-    const int skip = uniform(run) * P;
+    const int skip = uniform(ref.run) * P;
     it.p0 += skip;
     it.n = min(P, it.n - skip);
   }
