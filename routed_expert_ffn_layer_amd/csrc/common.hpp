@@ -195,4 +195,80 @@ __device__ __forceinline__ ItemRef nth_item(const int32_t* __restrict__ offsets,
   return nth_item_t<16, RUNS>(offsets, slot_of_expert, expert_addr, E, a, P);
 }
 
+// Routed expert of rank r when the active experts are ordered longest first: by
+// their number of 32-token tiles, ceil(n / 32), descending, then by ascending id
+// (same loads and the same ItemRef as nth_item; expert -1 if fewer than r+1
+// experts are active).  Each round takes the largest tile count left below the
+// previous one, so the loop ends after at most as many rounds as there are
+// distinct counts, and every active expert has exactly one rank.
+template <int EPL>
+__device__ __forceinline__ ItemRef nth_longest_t(const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ slot_of_expert,
+                                                 const uint64_t* __restrict__ expert_addr, int E, int r) {
+  const int lane = threadIdx.x & 63;
+  int lo[EPL], hi[EPL], sl[EPL], c[EPL];
+  uint64_t ad[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = i * 64 + lane;
+    const bool in = e < E;
+    lo[i] = in ? offsets[e] : 0;
+    hi[i] = in ? offsets[e + 1] : 0;
+    ad[i] = 0;
+    if (expert_addr) {
+      ad[i] = in ? expert_addr[e] : 0;
+      sl[i] = ad[i] != 0 ? 0 : -1;
+    } else {
+      sl[i] = in ? slot_of_expert[e] : -1;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) c[i] = (hi[i] > lo[i] && sl[i] >= 0) ? (hi[i] - lo[i] + 31) >> 5 : 0;
+  ItemRef ref;
+  int base = 0, bound = 0x7fffffff;
+  for (;;) {
+    int m = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) m = max(m, c[i] < bound ? c[i] : 0);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d, 64));
+    if (m == 0) break;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const uint64_t bits = __ballot(c[i] == m);
+      const int cnt = __popcll(bits);
+      if (r < base + cnt) {
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u));
+        const int owner = __builtin_ctzll(__ballot(c[i] == m && below == r - base));
+        ref.expert = i * 64 + owner;
+        ref.run = 0;
+        ref.lo = __shfl(lo[i], owner, 64);
+        ref.hi = __shfl(hi[i], owner, 64);
+        ref.slot = __shfl(sl[i], owner, 64);
+        ref.addr = expert_addr ? ((uint64_t)(uint32_t)__shfl((int)(uint32_t)(ad[i] >> 32), owner, 64) << 32) |
+                                     (uint32_t)__shfl((int)(uint32_t)ad[i], owner, 64)
+                               : 0;
+        return ref;
+      }
+      base += cnt;
+    }
+    bound = m;
+  }
+  ref.expert = -1;
+  ref.run = ref.lo = ref.hi = ref.slot = 0;
+  ref.addr = 0;
+  return ref;
+}
+
+__device__ __forceinline__ ItemRef nth_longest(const int32_t* __restrict__ offsets,
+                                               const int32_t* __restrict__ slot_of_expert,
+                                               const uint64_t* __restrict__ expert_addr, int E, int r) {
+  if (E <= 64) return nth_longest_t<1>(offsets, slot_of_expert, expert_addr, E, r);
+  if (E <= 128) return nth_longest_t<2>(offsets, slot_of_expert, expert_addr, E, r);
+  if (E <= 256) return nth_longest_t<4>(offsets, slot_of_expert, expert_addr, E, r);
+  if (E <= 512) return nth_longest_t<8>(offsets, slot_of_expert, expert_addr, E, r);
+  return nth_longest_t<16>(offsets, slot_of_expert, expert_addr, E, r);
+}
+
 }  // namespace moe

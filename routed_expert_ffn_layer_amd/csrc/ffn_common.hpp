@@ -78,6 +78,30 @@ __device__ __forceinline__ Item resolve_item_at(const FfnArgs& a, int b, int sha
   return it;
 }
 
+// Grouped-GEMM order (no shared expert): block b runs on XCD b % 8, in dispatch
+// order; the routed experts ranked longest first (nth_longest) are dealt round
+// robin over the XCDs, rank r to XCD r % 8 at item position r / 8 there, so every
+// XCD gets an even share of the work and starts its longest items first (shortest
+// last, so its CUs finish close together); the routed_tiles blocks of one item stay
+// consecutive on one XCD.  The grid is 8 * ceil(items / 8) * routed_tiles blocks.
+__device__ __forceinline__ Item resolve_item_longest(const FfnArgs& a, int routed_tiles) {
+  Item it;
+  const int x = blockIdx.x % 8, q = blockIdx.x / 8;
+  const int pos = q / routed_tiles;
+  it.tile = q - pos * routed_tiles;
+  it.shared = false;
+  const ItemRef ref = nth_longest(a.offsets, a.slot_of_expert, a.expert_addr, a.E, pos * 8 + x);
+  it.valid = uniform(ref.expert) >= 0;
+  if (!it.valid) return it;
+  it.w = a.expert_addr ? uniform(reinterpret_cast<const uint8_t*>(ref.addr))
+                       : uniform(a.slot_pool + (uint64_t)uniform(ref.slot) * a.slot_stride);
+  it.I = a.I;
+  it.p0 = uniform(ref.lo);
+  it.n = uniform(ref.hi) - it.p0;
+  it.hrow0 = it.p0;
+  return it;
+}
+
 template <bool SPLIT = false>
 __device__ __forceinline__ Item resolve_item(const FfnArgs& a, int shared_tiles, int routed_tiles) {
   return resolve_item_at<SPLIT>(a, blockIdx.x, shared_tiles, routed_tiles);

@@ -43,7 +43,10 @@
 // 16x16x32 design 1080-1091 us; later, on another box, the scales in LDS 938-941 us
 // against 959 us for the per-chunk scale loads (913 us with no scale loads at all).
 // Blocks are ordered so that the blocks of one expert run together on one XCD
-// (blockIdx b executes on XCD b % 8), keeping its token rows in that XCD's L2.
+// (blockIdx b executes on XCD b % 8), keeping its token rows in that XCD's L2, and
+// (without a shared expert) the experts go longest first, dealt round robin over
+// the XCDs: each XCD gets an even share of the token tiles and ends on its shortest
+// items, instead of a run of ascending ids whose last blocks leave CUs idle.
 #include "ffn_common.hpp"
 #include "kernels.hpp"
 
@@ -478,12 +481,18 @@ struct GGrid {
   int tiles_per_block;                 // 32-row tiles per block (4 R)
   int shared_tiles, routed_tiles;      // 32-row tiles per item
   int shared_blocks, routed_blocks;    // blocks per item
+  int longest;                         // items longest first, round robin over the XCDs (no shared expert)
 };
+
+__device__ __forceinline__ Item g_item(const FfnArgs& a, const GGrid& gr) {
+  return gr.longest ? resolve_item_longest(a, gr.routed_blocks)
+                    : resolve_item_at(a, xcd_logical_block(), gr.shared_blocks, gr.routed_blocks);
+}
 
 template <typename CF>
 __global__ __launch_bounds__(CF::W * 64) __attribute__((amdgpu_waves_per_eu(CF::W / 4, CF::W / 4))) void grouped_gate_up(
     FfnArgs a, GGrid gr) {
-  const Item it = resolve_item_at(a, xcd_logical_block(), gr.shared_blocks, gr.routed_blocks);
+  const Item it = g_item(a, gr);
   if (!it.valid) return;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[CF::LDS];
   constexpr int R = CF::R, WT = CF::WT;
@@ -528,7 +537,7 @@ __global__ __launch_bounds__(CF::W * 64) __attribute__((amdgpu_waves_per_eu(CF::
 template <typename CF>
 __global__ __launch_bounds__(CF::W * 64) __attribute__((amdgpu_waves_per_eu(CF::W / 4, CF::W / 4))) void grouped_down(
     FfnArgs a, GGrid gr) {
-  const Item it = resolve_item_at(a, xcd_logical_block(), gr.shared_blocks, gr.routed_blocks);
+  const Item it = g_item(a, gr);
   if (!it.valid) return;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[CF::LDS];
   constexpr int R = CF::R, WT = CF::WT;
@@ -566,9 +575,17 @@ bool prefill_supported(int wtype, int H, int I, int I_shared) {
 
 static unsigned pad8(unsigned g) { return (g + 7) / 8 * 8; }
 
+// Blocks of a launch: longest-first order, ceil(items / 8) items per XCD; else the
+// shared expert's blocks and every item's, padded to a multiple of 8.
+static unsigned g_blocks(const GGrid& gr, int routed_items) {
+  if (gr.longest) return 8u * (unsigned)((routed_items + 7) / 8) * (unsigned)gr.routed_blocks;
+  return pad8(gr.shared_blocks + routed_items * gr.routed_blocks);
+}
+
 template <typename CF>
 static GGrid g_grid(int routed_tiles, int shared_tiles) {
   GGrid g;
+  g.longest = shared_tiles == 0;
   g.tiles_per_block = CF::W * CF::R;
   g.routed_tiles = routed_tiles;
   g.shared_tiles = shared_tiles;
@@ -581,7 +598,7 @@ template <typename CF>
 static hipError_t launch_gu(const FfnArgs& a, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   const GGrid gr = g_grid<CF>(a.I / 16, a.shared_w ? a.I_shared / 16 : 0);
-  const unsigned grid = pad8(gr.shared_blocks + a.routed_items * gr.routed_blocks);
+  const unsigned grid = g_blocks(gr, a.routed_items);
   hipLaunchKernelGGL(grouped_gate_up<CF>, dim3(grid), dim3(CF::W * 64), 0, st, a, gr);
   return hipGetLastError();
 }
@@ -591,7 +608,7 @@ static hipError_t launch_dn(const FfnArgs& a, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   const int tiles = a.H / 32;
   const GGrid gr = g_grid<CF>(tiles, a.shared_w ? tiles : 0);
-  const unsigned grid = pad8(gr.shared_blocks + a.routed_items * gr.routed_blocks);
+  const unsigned grid = g_blocks(gr, a.routed_items);
   hipLaunchKernelGGL(grouped_down<CF>, dim3(grid), dim3(CF::W * 64), 0, st, a, gr);
   return hipGetLastError();
 }
