@@ -437,8 +437,12 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* coun
 // ---------------------------------------------------------------------------
 // Combine: y[t] = sum_j w[t][j] * rows[inv[t*k+j]] (+ shared[t]), f32 fused
 // multiply-add in increasing j, then one rounding to the output type.  Each
-// thread owns 4 consecutive columns of one token.
+// thread owns 4 consecutive columns of one token.  The pairs go in groups of 8:
+// every index, weight and row of a group is requested before the group's first
+// multiply-add (one memory round trip per group instead of two per pair), then
+// the group is added in increasing j, the same operations in the same order.
 // ---------------------------------------------------------------------------
+constexpr int kCombineGroup = 8;
 template <bool BF16OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ rows, const float* __restrict__ w,
                                                       const int32_t* __restrict__ inv,
@@ -448,19 +452,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = blockIdx.x / cb;
   const int c4 = (blockIdx.x % cb) * 256 + threadIdx.x;
   if (c4 * 4 >= H) return;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (shared) s = reinterpret_cast<const float4*>(shared + (size_t)t * H)[c4];
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int p = inv[(size_t)t * k + j];
-    if (p < 0) continue;  // pair dropped by the permutation (expert id out of range)
-    const float wj = w[(size_t)t * k + j];
-    const float4 o = reinterpret_cast<const float4*>(rows + (size_t)p * H)[c4];
-    acc.x = fmaf(wj, o.x, acc.x);
-    acc.y = fmaf(wj, o.y, acc.y);
-    acc.z = fmaf(wj, o.z, acc.z);
-    acc.w = fmaf(wj, o.w, acc.w);
+  for (int j0 = 0; j0 < k; j0 += kCombineGroup) {
+    int p[kCombineGroup];
+    float wj[kCombineGroup];
+    float4 o[kCombineGroup];
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u) {
+      const int j = j0 + u;
+      p[u] = j < k ? inv[(size_t)t * k + j] : -1;  // -1: no pair, or dropped by the permutation
+      wj[u] = j < k ? w[(size_t)t * k + j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u)
+      o[u] = p[u] >= 0 ? reinterpret_cast<const float4*>(rows + (size_t)p[u] * H)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u) {
+      if (p[u] < 0) continue;
+      acc.x = fmaf(wj[u], o[u].x, acc.x);
+      acc.y = fmaf(wj[u], o[u].y, acc.y);
+      acc.z = fmaf(wj[u], o[u].z, acc.z);
+      acc.w = fmaf(wj[u], o[u].w, acc.w);
+    }
   }
   if (shared) {
-    const float4 s = reinterpret_cast<const float4*>(shared + (size_t)t * H)[c4];
     acc.x += s.x;
     acc.y += s.y;
     acc.z += s.z;
