@@ -652,7 +652,7 @@ size_t ffn_workspace_bytes(int wtype, int T, int k, int H, int I, int I_shared) 
 // (decode shapes: bf16 H=2048/I=512, MXFP4 H=4096/I=2048; T = 1 .. 64):
 //   gate_up bf16   T <= 4: KW=4, R=1   else KW=2, R=1
 //   gate_up MXFP4  T <= 16: KW=1, R=2  else KW=1, R=4
-//   down    bf16   KW=1, R=2
+//   down    bf16   T = 1: KW=2, R=1   else KW=1, R=2
 //   down    MXFP4  T <= 16: KW=1, R=2  else KW=1, R=4
 struct Shape {
   int kw, r;
@@ -662,9 +662,11 @@ static Shape gate_up_shape(int wtype, int T) {
   if (wtype == W_BF16) return T <= 4 ? Shape{4, 1} : Shape{2, 1};
   return T <= 16 ? Shape{1, kDecMx1R} : Shape{1, kDecMxNR};
 }
-constexpr int kDecBf16DnKw = 1, kDecBf16DnR = 2;  // bf16 down: waves splitting K, row tiles
+// bf16 down: one token's few experts fill the GPU only with K split over 2 waves of
+// one row tile each (T = 1: 5% faster per layer); larger batches take 2 row tiles
+// per wave over the whole K.
 static Shape down_shape(int wtype, int T) {
-  if (wtype == W_BF16) return Shape{kDecBf16DnKw, kDecBf16DnR};
+  if (wtype == W_BF16) return T == 1 ? Shape{2, 1} : Shape{1, 2};
   return T <= 16 ? Shape{1, kDecMx1R} : Shape{1, kDecMxNR};
 }
 
@@ -782,7 +784,10 @@ hipError_t launch_ffn_down(int wtype, const FfnArgs& a, hipStream_t st) {
   const int shared_tiles = sh ? tiles : 0;
   const unsigned grid = shared_tiles * shared_items(a.T, b.pass_rows) + b.routed_items * tiles;
   if (!grid) return hipSuccess;
-  if (wtype == W_BF16) dn_nt<W_BF16, kDecBf16DnKw, kDecBf16DnR>(b, st, grid, shared_tiles, tiles);
+  if (wtype == W_BF16) {
+    if (sp.kw == 2) dn_nt<W_BF16, 2, 1>(b, st, grid, shared_tiles, tiles);
+    else dn_nt<W_BF16, 1, 2>(b, st, grid, shared_tiles, tiles);
+  }
   else if (sp.r == 1) dn_nt<W_MXFP4, 1, 1>(b, st, grid, shared_tiles, tiles);
   else if (sp.r == 2) dn_nt<W_MXFP4, 1, 2>(b, st, grid, shared_tiles, tiles);
   else dn_nt<W_MXFP4, 1, 4>(b, st, grid, shared_tiles, tiles);
