@@ -671,6 +671,11 @@ static Shape down_shape(int wtype, int T) {
 }
 
 constexpr int kDecMxNtMax = 2;  // MXFP4: token tiles per pass
+// The MXFP4 launchers build one kernel family per row-tile count of the shape
+// table: kDecMx1R row tiles with one-tile passes (T <= 16), kDecMxNR with two.
+static_assert(kDecMxNtMax == 2 && kDecMx1R != kDecMxNR, "MXFP4 decode shapes: (kDecMx1R, 1 tile), (kDecMxNR, 2 tiles)");
+template <int WT, int R>
+constexpr int mx_nt() { return R == kDecMx1R ? 1 : 2; }
 static int pick_nt(int T, int wtype) {
   const int nt = T <= 16 ? 1 : T <= 32 ? 2 : T <= 64 ? 4 : 8;
   return wtype == W_MXFP4 && nt > kDecMxNtMax ? kDecMxNtMax : nt;
@@ -714,16 +719,22 @@ static void gu_nt(const FfnArgs& a0, hipStream_t st, unsigned grid, int sh, int 
   FfnArgs a = a0;
   a.lds_rows = WT == W_MXFP4 && KW == 1 ? lds_rows_for(a.T, a.H) : 0;
   const size_t lb = (size_t)a.lds_rows * ((size_t)a.H * 2 + 16);
-  switch (pick_nt(a.T, WT)) {
-    case 1:
+  if constexpr (WT == W_MXFP4) {  // the pass width the shape table pairs with R
+    if constexpr (mx_nt<WT, R>() == 1) {
       if (a.lds_rows > 0)
-        launch_dec_kernel<WT, 1>(gate_up_mfma<WT, 1, KW, R, WT == W_MXFP4 && KW == 1>, grid, lb, st, a, sh, rt);
+        launch_dec_kernel<WT, 1>(gate_up_mfma<WT, 1, KW, R, KW == 1>, grid, lb, st, a, sh, rt);
       else
         launch_dec_kernel<WT, 1>(gate_up_mfma<WT, 1, KW, R>, grid, 0, st, a, sh, rt);
-      break;
-    case 2: launch_dec_kernel<WT, 2>(gate_up_mfma<WT, 2, KW, R>, grid, 0, st, a, sh, rt); break;
-    case 4: launch_dec_kernel<WT, 4>(gate_up_mfma<WT, 4, KW, R>, grid, 0, st, a, sh, rt); break;
-    default: launch_dec_kernel<WT, 8>(gate_up_mfma<WT, 8, KW, R>, grid, 0, st, a, sh, rt); break;
+    } else {
+      launch_dec_kernel<WT, 2>(gate_up_mfma<WT, 2, KW, R>, grid, 0, st, a, sh, rt);
+    }
+  } else {
+    switch (pick_nt(a.T, WT)) {
+      case 1: launch_dec_kernel<WT, 1>(gate_up_mfma<WT, 1, KW, R>, grid, 0, st, a, sh, rt); break;
+      case 2: launch_dec_kernel<WT, 2>(gate_up_mfma<WT, 2, KW, R>, grid, 0, st, a, sh, rt); break;
+      case 4: launch_dec_kernel<WT, 4>(gate_up_mfma<WT, 4, KW, R>, grid, 0, st, a, sh, rt); break;
+      default: launch_dec_kernel<WT, 8>(gate_up_mfma<WT, 8, KW, R>, grid, 0, st, a, sh, rt); break;
+    }
   }
 }
 template <int WT, int KW, int R>
@@ -732,16 +743,22 @@ static void dn_nt(const FfnArgs& a0, hipStream_t st, unsigned grid, int sh, int 
   const int kmax = a.I > a.I_shared ? a.I : a.I_shared;
   a.lds_rows = WT == W_MXFP4 && KW == 1 ? lds_rows_for(a.T, kmax) : 0;
   const size_t lb = (size_t)a.lds_rows * ((size_t)kmax * 2 + 16);
-  switch (pick_nt(a.T, WT)) {
-    case 1:
+  if constexpr (WT == W_MXFP4) {  // the pass width the shape table pairs with R
+    if constexpr (mx_nt<WT, R>() == 1) {
       if (a.lds_rows > 0)
-        launch_dec_kernel<WT, 1>(down_mfma<WT, 1, KW, R, WT == W_MXFP4 && KW == 1>, grid, lb, st, a, sh, rt);
+        launch_dec_kernel<WT, 1>(down_mfma<WT, 1, KW, R, KW == 1>, grid, lb, st, a, sh, rt);
       else
         launch_dec_kernel<WT, 1>(down_mfma<WT, 1, KW, R>, grid, 0, st, a, sh, rt);
-      break;
-    case 2: launch_dec_kernel<WT, 2>(down_mfma<WT, 2, KW, R>, grid, 0, st, a, sh, rt); break;
-    case 4: launch_dec_kernel<WT, 4>(down_mfma<WT, 4, KW, R>, grid, 0, st, a, sh, rt); break;
-    default: launch_dec_kernel<WT, 8>(down_mfma<WT, 8, KW, R>, grid, 0, st, a, sh, rt); break;
+    } else {
+      launch_dec_kernel<WT, 2>(down_mfma<WT, 2, KW, R>, grid, 0, st, a, sh, rt);
+    }
+  } else {
+    switch (pick_nt(a.T, WT)) {
+      case 1: launch_dec_kernel<WT, 1>(down_mfma<WT, 1, KW, R>, grid, 0, st, a, sh, rt); break;
+      case 2: launch_dec_kernel<WT, 2>(down_mfma<WT, 2, KW, R>, grid, 0, st, a, sh, rt); break;
+      case 4: launch_dec_kernel<WT, 4>(down_mfma<WT, 4, KW, R>, grid, 0, st, a, sh, rt); break;
+      default: launch_dec_kernel<WT, 8>(down_mfma<WT, 8, KW, R>, grid, 0, st, a, sh, rt); break;
+    }
   }
 }
 
@@ -764,9 +781,8 @@ hipError_t launch_ffn_gate_up(int wtype, const FfnArgs& a, hipStream_t st) {
     if (sp.kw == 4) gu_nt<W_BF16, 4, 1>(b, st, grid, shared_tiles, routed_tiles);
     else gu_nt<W_BF16, 2, 1>(b, st, grid, shared_tiles, routed_tiles);
   } else {
-    if (sp.r == 1) gu_nt<W_MXFP4, 1, 1>(b, st, grid, shared_tiles, routed_tiles);
-    else if (sp.r == 2) gu_nt<W_MXFP4, 1, 2>(b, st, grid, shared_tiles, routed_tiles);
-    else gu_nt<W_MXFP4, 1, 4>(b, st, grid, shared_tiles, routed_tiles);
+    if (sp.r == kDecMx1R) gu_nt<W_MXFP4, 1, kDecMx1R>(b, st, grid, shared_tiles, routed_tiles);
+    else gu_nt<W_MXFP4, 1, kDecMxNR>(b, st, grid, shared_tiles, routed_tiles);
   }
   return hipGetLastError();
 }
@@ -792,9 +808,8 @@ hipError_t launch_ffn_down(int wtype, const FfnArgs& a, hipStream_t st) {
     if (sp.kw == 2) dn_nt<W_BF16, 2, 1>(b, st, grid, shared_tiles, tiles);
     else dn_nt<W_BF16, 1, 2>(b, st, grid, shared_tiles, tiles);
   }
-  else if (sp.r == 1) dn_nt<W_MXFP4, 1, 1>(b, st, grid, shared_tiles, tiles);
-  else if (sp.r == 2) dn_nt<W_MXFP4, 1, 2>(b, st, grid, shared_tiles, tiles);
-  else dn_nt<W_MXFP4, 1, 4>(b, st, grid, shared_tiles, tiles);
+  else if (sp.r == kDecMx1R) dn_nt<W_MXFP4, 1, kDecMx1R>(b, st, grid, shared_tiles, tiles);
+  else dn_nt<W_MXFP4, 1, kDecMxNR>(b, st, grid, shared_tiles, tiles);
   return hipGetLastError();
 }
 
