@@ -10,7 +10,7 @@ import torch
 
 import synth
 from helpers import (BF16_REL, F32_ATOL, W_ATOL, W_RTOL, assert_close_abs, assert_close_bf16_output, assert_close_rel,
-                     bf16_to_f64,
+                     bf16_rne, bf16_to_f64,
                      check_bf16_output, combine_f32, dev, log, pool_from_experts, run_resident_layer, to_dev)
 from routed_expert_ffn_layer_amd import layer as L
 from routed_expert_ffn_layer_amd import moe
@@ -213,6 +213,48 @@ def test_small_layers(ora, case):
     ref = _check_layer(ora, lay, b)
     counts = np.bincount(ref["ids"].ravel(), minlength=E)
     log(f"  tokens per expert {sorted(counts.tolist())}")
+
+
+# (T, k, H, shared): the combine requests its pairs in groups of 8, so k covers one
+# pair, a part group, exactly one group, one more than a group, several groups with a
+# part group at the end, and the largest k the library takes.
+COMBINE_CASES = [(3, 1, 256, False), (5, 7, 512, True), (4, 8, 2048, False), (6, 9, 1024, True),
+                 (2, 20, 4096, True), (3, 32, 256, False)]
+
+
+@pytest.mark.parametrize("T,k,H,shared", COMBINE_CASES, ids=lambda v: str(v))
+def test_combine_pair_groups(ora, T, k, H, shared):
+    """y[t] = sum_j w[t][j] * rows[inv[t*k+j]] (+ shared[t]) over whole and part groups of
+    pairs, with about a tenth of the pairs dropped (inv = -1, as for expert ids out of
+    range), against the oracle's combine of the same rows; the bf16 output is the
+    round-to-nearest-even of the f32 one."""
+    g = np.random.default_rng(7000 + T * 100 + k)
+    n = T * k
+    out_rows = g.standard_normal((n, H)).astype(np.float32)
+    w = g.random((T, k)).astype(np.float32)
+    inv = g.permutation(n).astype(np.int32)
+    inv[g.random(n) < 0.1] = -1
+    sh = g.standard_normal((T, H)).astype(np.float32) if shared else None
+    rows_ref = np.zeros((n, H))
+    rows_ref[inv >= 0] = out_rows[inv[inv >= 0]]
+    y_ref = ora.combine(rows_ref, w, sh)
+    y32 = torch.empty((T, H), dtype=torch.float32, device=dev())
+    y16 = torch.empty((T, H), dtype=torch.bfloat16, device=dev())
+    args = (to_dev(out_rows), to_dev(w), to_dev(inv), to_dev(sh) if shared else None)
+    moe.moe_combine(*args, y32, moe.MOE_F32)
+    moe.moe_combine(*args, y16, moe.MOE_BF16)
+    torch.cuda.synchronize()
+    got = y32.cpu().numpy().astype(np.float64)
+    # f32 multiply-adds in a fixed order: each output within (k + 2) units of f32
+    # rounding of the sum of the magnitudes it adds up
+    mag = np.abs(w.astype(np.float64)[:, :, None] * rows_ref.reshape(T, k, H)).sum(axis=1)
+    if shared:
+        mag += np.abs(sh)
+    bound = (k + 2) * 2.0 ** -24 * mag + 1e-30
+    err = np.abs(got - y_ref)
+    log(f"combine T={T} k={k} H={H} shared={shared}: max err / bound = {float((err / bound).max()):.3f}")
+    assert (err <= bound).all(), f"max err / bound {float((err / bound).max())}"
+    np.testing.assert_array_equal(bf16_to_f64(y16), bf16_rne(got))
 
 
 def test_decode_bf16_full_shape(ora):
